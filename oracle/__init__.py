@@ -1,0 +1,194 @@
+"""fp64 CPU oracle for causal sliding-window attention (TEST INFRASTRUCTURE).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and this
+package never imports the product: the two share no code.
+
+The arithmetic lives in ``swa_oracle.c`` (plain loops, fp64, OpenMP over rows);
+this module only compiles it with gcc and marshals numpy arrays through ctypes.
+Every function takes and returns float64 arrays in the layout the C file
+documents ([B][heads][rows][d], d fastest).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "swa_oracle.c")
+LIB = os.path.join(_HERE, "libswa_oracle.so")
+_lock = threading.Lock()
+_default = None
+
+STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full",
+              "n_partial")
+
+
+def build(force: bool = False, src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, strict IEEE: no fast-math, no
+    FMA contraction).  Rebuilds when the source is newer than the library."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes front of one compiled oracle library (float64 numpy in and out)."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        d = ctypes.c_double
+        lib.orc_fwd.argtypes = [i, i, i, i, i, i, P, P, P, P, d, P]
+        lib.orc_fwd.restype = None
+        lib.orc_fwd_rows.argtypes = [i, i, i, i, i, i, P, P, P, P, d, i, P, P, P, P]
+        lib.orc_fwd_rows.restype = None
+        lib.orc_chunk.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, P, d, P]
+        lib.orc_chunk.restype = None
+        lib.orc_decode.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, P, d, P]
+        lib.orc_decode.restype = None
+        lib.orc_blockmask.argtypes = [i, i, i, i, i, i, P, P, P, P, i, P, P, P,
+                                      P, P, P, P, P]
+        lib.orc_blockmask.restype = ctypes.c_int64
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = lib_path
+
+    def num_threads(self) -> int:
+        return self.lib.orc_num_threads()
+
+    def fwd(self, q, k, v, W: int, scale: float, q_len=None) -> np.ndarray:
+        """Full-sequence SWA forward.  q [B,H,N,d], k/v [B,Hkv,N,d] -> o [B,H,N,d]."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, N, dd = q.shape
+        Hkv = k.shape[1]
+        ql = _i32(q_len)
+        o = np.empty_like(q)
+        self.lib.orc_fwd(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(ql),
+                         float(scale), _ptr(o))
+        return o
+
+    def fwd_rows(self, q, k, v, W: int, scale: float, rows, q_len=None) -> np.ndarray:
+        """Forward for selected rows only.  rows: int array [n,3] of (b, h, i)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, N, dd = q.shape
+        Hkv = k.shape[1]
+        rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
+        rb, rh, ri = (np.ascontiguousarray(rows[:, c]) for c in range(3))
+        ql = _i32(q_len)
+        out = np.empty((rows.shape[0], dd), dtype=np.float64)
+        self.lib.orc_fwd_rows(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(ql),
+                              float(scale), rows.shape[0], _ptr(rb), _ptr(rh), _ptr(ri),
+                              _ptr(out))
+        return out
+
+    def chunk(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
+              W: int, scale: float):
+        """Chunked prefill against a ring cache.  Returns (o, k_cache', v_cache',
+        ring_start', cache_len', next_pos'); the inputs are not modified."""
+        q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+        kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+        rs, cl, npos = (_i32(x).copy() for x in (ring_start, cache_len, next_pos))
+        B, H, Tq, dd = q.shape
+        Hkv = kn.shape[1]
+        o = np.empty_like(q)
+        self.lib.orc_chunk(B, H, Hkv, Tq, dd, W, _ptr(q), _ptr(kn), _ptr(vn), _ptr(kc),
+                           _ptr(vc), _ptr(rs), _ptr(cl), _ptr(npos), float(scale), _ptr(o))
+        return o, kc, vc, rs, cl, npos
+
+    def decode(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
+               W: int, scale: float):
+        """One decode step (append, then attend).  q [B,H,d], k_new/v_new [B,Hkv,d].
+        Returns (o, k_cache', v_cache', ring_start', cache_len', next_pos')."""
+        q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+        kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+        rs, cl, npos = (_i32(x).copy() for x in (ring_start, cache_len, next_pos))
+        B, H, dd = q.shape
+        Hkv = kn.shape[1]
+        o = np.empty_like(q)
+        self.lib.orc_decode(B, H, Hkv, dd, W, _ptr(q), _ptr(kn), _ptr(vn), _ptr(kc),
+                            _ptr(vc), _ptr(rs), _ptr(cl), _ptr(npos), float(scale), _ptr(o))
+        return o, kc, vc, rs, cl, npos
+
+    def blockmask(self, B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=None,
+                  q_len=None, k_len=None, W_ring=0, ring_start=None, cache_len=None,
+                  next_pos=None):
+        """Brute-force block metadata.  Returns a dict with cls [B,nqt,nkt] uint8,
+        row_ptr [B*nqt+1] int32, col [nnz] int32, col_cls [nnz] uint8 and the six
+        statistics named in STAT_NAMES."""
+        nk = W_ring + nk_lin
+        nqt = -(-nq // tile_q)
+        nkt = -(-nk // tile_k)
+        cls = np.zeros((B, nqt, nkt), dtype=np.uint8)
+        row_ptr = np.zeros(B * nqt + 1, dtype=np.int32)
+        cap = max(1, B * nqt * nkt)
+        col = np.zeros(cap, dtype=np.int32)
+        col_cls = np.zeros(cap, dtype=np.uint8)
+        stats = np.zeros(6, dtype=np.int64)
+        qs, ks, ql, kl, rs, cl, npos = (_i32(x) for x in (
+            q_start, k_start, q_len, k_len, ring_start, cache_len, next_pos))
+        nnz = self.lib.orc_blockmask(B, nq, nk_lin, W, tile_q, tile_k, _ptr(qs), _ptr(ks),
+                                     _ptr(ql), _ptr(kl), W_ring, _ptr(rs), _ptr(cl),
+                                     _ptr(npos), _ptr(cls), _ptr(row_ptr), _ptr(col),
+                                     _ptr(col_cls), _ptr(stats))
+        out = {"cls": cls, "row_ptr": row_ptr, "col": col[:nnz].copy(),
+               "col_cls": col_cls[:nnz].copy()}
+        out.update({n: int(stats[i]) for i, n in enumerate(STAT_NAMES)})
+        return out
+
+
+def default() -> Oracle:
+    """The oracle built from swa_oracle.c next to this file."""
+    global _default
+    with _lock:
+        if _default is None:
+            _default = Oracle(build())
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def fwd(*a, **kw):
+    return default().fwd(*a, **kw)
+
+
+def fwd_rows(*a, **kw):
+    return default().fwd_rows(*a, **kw)
+
+
+def chunk(*a, **kw):
+    return default().chunk(*a, **kw)
+
+
+def decode(*a, **kw):
+    return default().decode(*a, **kw)
+
+
+def blockmask(*a, **kw):
+    return default().blockmask(*a, **kw)

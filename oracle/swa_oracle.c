@@ -1,0 +1,438 @@
+/*
+ * swa_oracle.c -- plain fp64 CPU oracle for causal sliding-window attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU library: it is written straight from
+ * the pages' statement of the method and is deliberately slow and literal.
+ *
+ * Sources (cited by page title and section):
+ *   [M003]  "Weight sparsity vs attention sparsity" (AI-infra knowledge base,
+ *           xuujii.github.io/ai-infra-kb/details/M003.html)
+ *   [Ch10]  "Chapter 10: local and sparse attention, SWA and DSA"
+ *           (LLMs-from-scratch book, book.ozine.me)
+ *   [Blog]  "Dense attention vs sliding-window sparse attention"
+ *           (maplevalley.com.cn/news/3171860)
+ *
+ * Conventions (readings where the pages leave a step open are marked READING):
+ *   - W counts the current token: query at logical position t may read keys at
+ *     logical positions max(0, t-W+1) .. t  [M003 §03], [Ch10 §10.1].
+ *   - scores s_j = scale * <q, k_j>; softmax is normalised over exactly the
+ *     allowed keys and the output is the weighted sum of their V rows
+ *     [M003 §03].  Keys are visited in ascending logical position.
+ *   - READING: a query with no allowed key (only padded rows) outputs 0; the
+ *     pages warn that such a row would otherwise give NaN [Ch10 §10.3].
+ *   - READING: grouped KV heads are contiguous groups, kv head = h / (H/Hkv).
+ *   - Tensors are row-major [B][heads][rows][d] with d fastest.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* The visibility rule of [M003 §03]: key j is visible from query i iff
+ * j <= i and j >= i-W+1.  Written on logical positions so that ring slots
+ * (whose physical index is not their position, [M003 §06]) use it unchanged.
+ * [Ch10 §10.1] states the same rule as: forbidden iff (i-j) < 0 or (i-j) >= W. */
+static int allowed(int64_t qpos, int64_t kpos, int64_t W)
+{
+    return kpos <= qpos && kpos >= qpos - W + 1;
+}
+
+/* Attention of one query row over a list of candidate keys given in ascending
+ * logical position.  Only keys passing allowed() take part; softmax is
+ * normalised over exactly those [M003 §03].  Two passes: the maximum score
+ * first, then exp(s - max), so that exp never overflows (the result is the
+ * same softmax).  scratch must hold nk doubles. */
+static void attend_row(int d, int64_t W, double scale,
+                       const double *q, int64_t qpos,
+                       int nk, const double *const *krow, const double *const *vrow,
+                       const int64_t *kpos, double *scratch, double *out)
+{
+    int c, j, any = 0;
+    double m = -INFINITY, l = 0.0;
+
+    for (c = 0; c < d; c++)
+        out[c] = 0.0;
+
+    /* s_j = scale * sum_c q_c k_jc for every allowed key */
+    for (j = 0; j < nk; j++) {
+        double s = 0.0;
+        if (!allowed(qpos, kpos[j], W))
+            continue;
+        for (c = 0; c < d; c++)
+            s += q[c] * krow[j][c];
+        s *= scale;
+        scratch[j] = s;
+        if (!any || s > m)
+            m = s;
+        any = 1;
+    }
+    if (!any)
+        return; /* READING: empty allowed set -> output 0 */
+
+    /* e_j = exp(s_j - m); l = sum e_j; o = sum e_j v_j / l */
+    for (j = 0; j < nk; j++) {
+        double e;
+        if (!allowed(qpos, kpos[j], W))
+            continue;
+        e = exp(scratch[j] - m);
+        l += e;
+        for (c = 0; c < d; c++)
+            out[c] += e * vrow[j][c];
+    }
+    for (c = 0; c < d; c++)
+        out[c] /= l;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Full-sequence forward.  Query row i and key row j sit at logical positions
+ * i and j.  q_len[b] (NULL = N) is the valid length of sequence b: rows and
+ * keys at or past it are padding.  Padded rows are written as 0 (READING).
+ * q: [B][H][N][d], k, v: [B][Hkv][N][d], o: [B][H][N][d]. */
+void orc_fwd(int B, int H, int Hkv, int N, int d, int W,
+             const double *q, const double *k, const double *v,
+             const int32_t *q_len, double scale, double *o)
+{
+    int64_t b, h;
+    const int G = H / Hkv;
+
+    for (b = 0; b < B; b++) {
+        const int len = q_len ? q_len[b] : N;
+        for (h = 0; h < H; h++) {
+            const int64_t g = h / G; /* READING: contiguous head groups */
+            const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+            const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+            int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+            for (i = 0; i < N; i++) {
+                const double *qi = q + ((b * H + h) * (int64_t)N + i) * d;
+                double *oi = o + ((b * H + h) * (int64_t)N + i) * d;
+                int c, j;
+                const double **kr;
+                const double **vr;
+                int64_t *kp;
+                double *sc;
+                if (i >= len) { /* padded row */
+                    for (c = 0; c < d; c++)
+                        oi[c] = 0.0;
+                    continue;
+                }
+                /* candidate keys: every valid key of the sequence, in order */
+                kr = malloc(sizeof(*kr) * (size_t)len);
+                vr = malloc(sizeof(*vr) * (size_t)len);
+                kp = malloc(sizeof(*kp) * (size_t)len);
+                sc = malloc(sizeof(*sc) * (size_t)len);
+                for (j = 0; j < len; j++) {
+                    kr[j] = kb + (int64_t)j * d;
+                    vr[j] = vb + (int64_t)j * d;
+                    kp[j] = j;
+                }
+                attend_row(d, W, scale, qi, i, len, kr, vr, kp, sc, oi);
+                free(kr); free(vr); free(kp); free(sc);
+            }
+        }
+    }
+}
+
+/* The same forward, for a list of selected rows only (for large inputs).
+ * Row r is (rb[r], rh[r], ri[r]); its output goes to o_rows + r*d. */
+void orc_fwd_rows(int B, int H, int Hkv, int N, int d, int W,
+                  const double *q, const double *k, const double *v,
+                  const int32_t *q_len, double scale,
+                  int nrows, const int32_t *rb, const int32_t *rh, const int32_t *ri,
+                  double *o_rows)
+{
+    int r;
+    const int G = H / Hkv;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < nrows; r++) {
+        const int64_t b = rb[r], h = rh[r], i = ri[r];
+        const int64_t g = h / G;
+        const int len = q_len ? q_len[b] : N;
+        const double *qi = q + ((b * H + h) * (int64_t)N + i) * d;
+        const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+        const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+        double *oi = o_rows + (int64_t)r * d;
+        int c, j;
+        const double **kr;
+        const double **vr;
+        int64_t *kp;
+        double *sc;
+        if (i >= len) {
+            for (c = 0; c < d; c++)
+                oi[c] = 0.0;
+            continue;
+        }
+        kr = malloc(sizeof(*kr) * (size_t)len);
+        vr = malloc(sizeof(*vr) * (size_t)len);
+        kp = malloc(sizeof(*kp) * (size_t)len);
+        sc = malloc(sizeof(*sc) * (size_t)len);
+        for (j = 0; j < len; j++) {
+            kr[j] = kb + (int64_t)j * d;
+            vr[j] = vb + (int64_t)j * d;
+            kp[j] = j;
+        }
+        attend_row(d, W, scale, qi, i, len, kr, vr, kp, sc, oi);
+        free(kr); free(vr); free(kp); free(sc);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ring-buffer cache [Blog §3.2]: a [heads][W][d] buffer per request plus a
+ * start index and a fill count.  While the fill count is below W a new row
+ * goes to the next free slot; once full it overwrites the slot at the start
+ * index, which then advances by one modulo W.  The free slot is taken as
+ * (start + len) mod W, which is the page's "slot len" when start is 0
+ * (READING).  next_pos counts logical positions appended so far, so the row
+ * in logical order r (0 = oldest) sits in slot (start + r) mod W at logical
+ * position next_pos - len + r: slots keep their original positions after
+ * being overwritten [M003 §06], [Ch10 §10.2]. */
+static void ring_append_one(int Hkv, int W, int d, double *kc, double *vc,
+                            int32_t *start, int32_t *len, int32_t *next_pos,
+                            const double *k_row_heads, const double *v_row_heads,
+                            int64_t head_stride)
+{
+    int slot, g;
+    if (*len < W) {
+        slot = (*start + *len) % W;
+        *len += 1;
+    } else {
+        slot = *start;
+        *start = (*start + 1) % W;
+    }
+    for (g = 0; g < Hkv; g++) {
+        memcpy(kc + ((int64_t)g * W + slot) * d, k_row_heads + g * head_stride,
+               sizeof(double) * (size_t)d);
+        memcpy(vc + ((int64_t)g * W + slot) * d, v_row_heads + g * head_stride,
+               sizeof(double) * (size_t)d);
+    }
+    *next_pos += 1;
+}
+
+/* Chunked prefill of Tq new tokens against the ring [Ch10 §10.2]:
+ * the old cache (old_len = cache_len rows, in logical order) is joined with
+ * the new rows; key positions start at next_pos - old_len, queries start at
+ * next_pos.  Every query attends over that union (which is why the step
+ * needs up to W+Tq-1 keys although only W stay cached).  Afterwards the new
+ * rows are appended to the ring one by one, so the ring keeps the last W.
+ * q: [B][H][Tq][d]; k_new, v_new: [B][Hkv][Tq][d];
+ * k_cache, v_cache: [B][Hkv][W][d] (in/out); ring state arrays [B] (in/out);
+ * o: [B][H][Tq][d]. */
+void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
+               const double *q, const double *k_new, const double *v_new,
+               double *k_cache, double *v_cache,
+               int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+               double scale, double *o)
+{
+    int b;
+    const int G = H / Hkv;
+    for (b = 0; b < B; b++) {
+        const int old_len = cache_len[b];
+        const int64_t p0 = next_pos[b];
+        const int nk = old_len + Tq;
+        int h, t;
+        for (h = 0; h < H; h++) {
+            const int64_t g = h / G;
+            const double *kc = k_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
+            const double *vc = v_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
+            const double *kn = k_new + ((int64_t)b * Hkv + g) * (int64_t)Tq * d;
+            const double *vn = v_new + ((int64_t)b * Hkv + g) * (int64_t)Tq * d;
+            const double **kr = malloc(sizeof(*kr) * (size_t)nk);
+            const double **vr = malloc(sizeof(*vr) * (size_t)nk);
+            int64_t *kp = malloc(sizeof(*kp) * (size_t)nk);
+            int r;
+            /* combined keys: old cache in logical order, then the new rows */
+            for (r = 0; r < old_len; r++) {
+                const int slot = (ring_start[b] + r) % W;
+                kr[r] = kc + (int64_t)slot * d;
+                vr[r] = vc + (int64_t)slot * d;
+                kp[r] = p0 - old_len + r; /* k_start_pos_abs = ptr - old_len */
+            }
+            for (t = 0; t < Tq; t++) {
+                kr[old_len + t] = kn + (int64_t)t * d;
+                vr[old_len + t] = vn + (int64_t)t * d;
+                kp[old_len + t] = p0 + t;
+            }
+#pragma omp parallel for schedule(dynamic, 4)
+            for (t = 0; t < Tq; t++) {
+                double *sc = malloc(sizeof(*sc) * (size_t)nk);
+                attend_row(d, W, scale,
+                           q + (((int64_t)b * H + h) * Tq + t) * d, p0 + t,
+                           nk, kr, vr, kp, sc,
+                           o + (((int64_t)b * H + h) * Tq + t) * d);
+                free(sc);
+            }
+            free(kr); free(vr); free(kp);
+        }
+        /* commit only after every query of the chunk has read the old ring */
+        for (t = 0; t < Tq; t++)
+            ring_append_one(Hkv, W, d,
+                            k_cache + (int64_t)b * Hkv * W * d,
+                            v_cache + (int64_t)b * Hkv * W * d,
+                            &ring_start[b], &cache_len[b], &next_pos[b],
+                            k_new + ((int64_t)b * Hkv * Tq + t) * d,
+                            v_new + ((int64_t)b * Hkv * Tq + t) * d,
+                            (int64_t)Tq * d);
+    }
+}
+
+/* One decode step: the new token's K/V row is appended to the ring first
+ * (READING: append, then attend, so the ring holds exactly the W positions
+ * the new query may see), then the query at the new token's position attends
+ * over the ring's valid slots taken in logical order.
+ * q: [B][H][d]; k_new, v_new: [B][Hkv][d]; cache and state as orc_chunk. */
+void orc_decode(int B, int H, int Hkv, int d, int W,
+                const double *q, const double *k_new, const double *v_new,
+                double *k_cache, double *v_cache,
+                int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                double scale, double *o)
+{
+    int b;
+    const int G = H / Hkv;
+    for (b = 0; b < B; b++) {
+        int64_t qpos;
+        int h, len;
+        ring_append_one(Hkv, W, d,
+                        k_cache + (int64_t)b * Hkv * W * d,
+                        v_cache + (int64_t)b * Hkv * W * d,
+                        &ring_start[b], &cache_len[b], &next_pos[b],
+                        k_new + (int64_t)b * Hkv * d, v_new + (int64_t)b * Hkv * d,
+                        (int64_t)d);
+        qpos = (int64_t)next_pos[b] - 1;
+        len = cache_len[b];
+#pragma omp parallel for schedule(static)
+        for (h = 0; h < H; h++) {
+            const int64_t g = h / G;
+            const double *kc = k_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
+            const double *vc = v_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
+            const double **kr = malloc(sizeof(*kr) * (size_t)len);
+            const double **vr = malloc(sizeof(*vr) * (size_t)len);
+            int64_t *kp = malloc(sizeof(*kp) * (size_t)len);
+            double *sc = malloc(sizeof(*sc) * (size_t)len);
+            int r;
+            for (r = 0; r < len; r++) {
+                const int slot = (ring_start[b] + r) % W;
+                kr[r] = kc + (int64_t)slot * d;
+                vr[r] = vc + (int64_t)slot * d;
+                kp[r] = (int64_t)next_pos[b] - len + r;
+            }
+            attend_row(d, W, scale, q + ((int64_t)b * H + h) * d, qpos,
+                       len, kr, vr, kp, sc, o + ((int64_t)b * H + h) * d);
+            free(kr); free(vr); free(kp); free(sc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block metadata by brute force [M003 §04]: every (query tile, key tile)
+ * pair is classified by counting the visible pairs among its coordinates:
+ * none -> skip (0), all in-range coordinates -> full (1), else partial (2).
+ * READING: tiles cut by the array edge count only their in-range area.
+ *
+ * Key axis: if W_ring > 0, keys 0..W_ring-1 are ring slots (positions from
+ * the ring state as in ring_append_one's comment; unfilled slots are
+ * invalid), followed by nk_lin linear keys.  Linear key t of batch b sits at
+ * k_start[b] + t and is valid iff t < k_len[b]; query i sits at q_start[b]+i
+ * and is valid iff i < q_len[b].  NULL position arrays mean 0, NULL length
+ * arrays mean "all valid".
+ *
+ * Outputs: cls[b][qt][kt]; CSR over rows b*nqt+qt in ascending key tile
+ * (row_ptr, col, col_cls); stats[6] = valid pairs, covered coordinates
+ * (in-range area of live blocks), distinct keys touched, live, full, partial
+ * blocks, each summed over b.  Returns the number of live blocks. */
+int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
+                      const int32_t *q_start, const int32_t *k_start,
+                      const int32_t *q_len, const int32_t *k_len,
+                      int W_ring, const int32_t *ring_start,
+                      const int32_t *cache_len, const int32_t *next_pos,
+                      uint8_t *cls, int32_t *row_ptr, int32_t *col,
+                      uint8_t *col_cls, int64_t *stats)
+{
+    const int nk = W_ring + nk_lin;
+    const int nqt = (nq + tile_q - 1) / tile_q;
+    const int nkt = (nk + tile_k - 1) / tile_k;
+    int64_t nnz = 0;
+    int b, s;
+    int64_t *qpos = malloc(sizeof(int64_t) * (size_t)(nq > 0 ? nq : 1));
+    int64_t *kpos = malloc(sizeof(int64_t) * (size_t)(nk > 0 ? nk : 1));
+    char *qok = malloc((size_t)(nq > 0 ? nq : 1));
+    char *kok = malloc((size_t)(nk > 0 ? nk : 1));
+    char *touched = malloc((size_t)(nk > 0 ? nk : 1));
+
+    for (s = 0; s < 6; s++)
+        stats[s] = 0;
+    row_ptr[0] = 0;
+
+    for (b = 0; b < B; b++) {
+        int i, j, qt, kt;
+        for (i = 0; i < nq; i++) {
+            qpos[i] = (q_start ? q_start[b] : 0) + (int64_t)i;
+            qok[i] = q_len ? (i < q_len[b]) : 1;
+        }
+        for (j = 0; j < W_ring; j++)
+            kok[j] = 0;
+        if (W_ring > 0) {
+            int r;
+            for (r = 0; r < cache_len[b]; r++) {
+                const int slot = (ring_start[b] + r) % W_ring;
+                kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r;
+                kok[slot] = 1;
+            }
+        }
+        for (j = 0; j < nk_lin; j++) {
+            kpos[W_ring + j] = (k_start ? k_start[b] : 0) + (int64_t)j;
+            kok[W_ring + j] = k_len ? (j < k_len[b]) : 1;
+        }
+        memset(touched, 0, (size_t)(nk > 0 ? nk : 1));
+
+        for (qt = 0; qt < nqt; qt++) {
+            const int i0 = qt * tile_q;
+            const int i1 = (i0 + tile_q < nq) ? i0 + tile_q : nq;
+            for (kt = 0; kt < nkt; kt++) {
+                const int j0 = kt * tile_k;
+                const int j1 = (j0 + tile_k < nk) ? j0 + tile_k : nk;
+                const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);
+                int64_t count = 0;
+                uint8_t c;
+                for (i = i0; i < i1; i++)
+                    for (j = j0; j < j1; j++)
+                        if (qok[i] && kok[j] && allowed(qpos[i], kpos[j], W)) {
+                            count++;
+                            touched[j] = 1;
+                        }
+                c = (count == 0) ? 0 : (count == area ? 1 : 2);
+                cls[((int64_t)b * nqt + qt) * nkt + kt] = c;
+                stats[0] += count;
+                if (c != 0) {
+                    col[nnz] = kt;
+                    col_cls[nnz] = c;
+                    nnz++;
+                    stats[1] += area;
+                    stats[3] += 1;
+                    stats[c == 1 ? 4 : 5] += 1;
+                }
+            }
+            row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;
+        }
+        for (j = 0; j < nk; j++)
+            stats[2] += touched[j];
+    }
+    free(qpos); free(kpos); free(qok); free(kok); free(touched);
+    return nnz;
+}
+
+/* Threads the OpenMP runtime will use (for reporting). */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,64 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies ``oracle/swa_oracle.c`` to a temporary directory, replaces one
+fragment with a plausible bug (an off-by-one window, a dropped term, a wrong
+index or operand, a ring bookkeeping slip), compiles it with gcc and runs the
+pins against it: at least one pin must fail.  Mutations are chosen so that the
+mutant never reads outside its arrays.
+"""
+import os
+
+import pytest
+
+import oracle
+from pins import PINS
+
+MUTANTS = {
+    # the window boundary read as (t - j) > W, the slip the SWA chapter warns of
+    "window_off_by_one": ("kpos >= qpos - W + 1;", "kpos >= qpos - W;"),
+    "no_causal_bound": ("return kpos <= qpos && kpos >= qpos - W + 1;",
+                        "return kpos >= qpos - W + 1;"),
+    "no_max_subtraction": ("e = exp(scratch[j] - m);", "e = exp(scratch[j]);"),
+    "scale_dropped": ("s *= scale;", "s *= 1.0;"),
+    "gqa_interleaved": ("h / G", "h % Hkv"),
+    "k_used_for_v": ("out[c] += e * vrow[j][c];", "out[c] += e * krow[j][c];"),
+    "no_normalisation": ("out[c] /= l;", "out[c] /= 1.0;"),
+    "chunk_key_position_shift": ("kp[r] = p0 - old_len + r;", "kp[r] = p0 - old_len + r + 1;"),
+    "chunk_query_position_shift": ("p0 + t,\n", "p0 + t + 1,\n"),
+    "ring_fill_ignores_start": ("slot = (*start + *len) % W;", "slot = *len % W;"),
+    "ring_start_not_advanced": ("*start = (*start + 1) % W;", "*start = *start % W;"),
+    "decode_query_position": ("qpos = (int64_t)next_pos[b] - 1;",
+                              "qpos = (int64_t)next_pos[b];"),
+    "decode_key_position_shift": ("kp[r] = (int64_t)next_pos[b] - len + r;",
+                                  "kp[r] = (int64_t)next_pos[b] - len + r - 1;"),
+    "padding_row_kept": ("if (i >= len) { /* padded row */", "if (i > len) {"),
+    "full_threshold": ("(count == area ? 1 : 2)", "(count * 2 >= area ? 1 : 2)"),
+    "edge_area_not_clipped": ("const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);",
+                              "const int64_t area = (int64_t)tile_q * tile_k;"),
+    "ring_slot_position_shift": ("kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r;",
+                                 "kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r + 1;"),
+    "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
+                          "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert old in src, "mutation anchor missing: %r" % old
+    mutated = src.replace(old, new)
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.build(force=True, src=path, out=os.path.join(str(tmp_path), "mutant.so"))
+    O = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(O)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, "no pin caught the planted mistake %s" % name
