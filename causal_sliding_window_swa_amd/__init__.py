@@ -1,1 +1,239 @@
-"""Causal sliding-window attention for MI355X (gfx950)."""
+"""Causal sliding-window attention for MI355X (gfx950): Python binding of libswa.so.
+
+Thin ctypes marshalling over the C ABI declared in ``include/swa.h``; every step
+of the computation runs in the library (host metadata builder, HIP kernels).
+PyTorch supplies device memory and streams only.  There is no fallback: when
+``libswa.so`` is missing or a call fails, a ``SwaError`` is raised.
+
+Functions keep the ABI's names:
+
+    swa_blockmask_size(B, nq, nk, tile_q, tile_k)          -> (cls_elems, max_nnz)
+    swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, ...) -> dict (host numpy)
+    swa_fwd(q, k, v, o, W, meta, tile_q, tile_k, q_len=None, scale=None)
+    swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len,
+                      next_pos, o, W, meta, tile_q, tile_k, scale=None)
+    swa_decode_workspace_size(B, H, d, W)
+    swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
+               o, workspace, W, scale=None)
+    swa_last_error()
+
+``meta`` is the device copy of a build (``meta_to_device``).  Calls are enqueued
+on torch's current stream of the tensors' device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswa.so")
+
+SWA_OK, SWA_EINVAL, SWA_EUNSUPPORTED, SWA_EHIP = 0, 1, 2, 3
+SWA_BF16, SWA_F32 = 0, 1
+STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full",
+              "n_partial")
+
+# Symbols declared in include/swa.h (checked by the CPU tests).
+EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
+           "swa_decode_workspace_size", "swa_decode", "swa_last_error")
+
+
+class SwaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("swa status %d: %s" % (code, msg))
+        self.code = code
+
+
+class MaskStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in STAT_NAMES]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded libswa.so (raises SwaError if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise SwaError(-1, "%s is missing: build it with "
+                               "`python -m causal_sliding_window_swa_amd.build`" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+            L.swa_blockmask_size.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_size_t)]
+            L.swa_blockmask_build.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P,
+                                              P, P, P, P, ctypes.POINTER(MaskStats)]
+            L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, F, P]
+            L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
+                                            P, P, P, P, F, P]
+            L.swa_decode_workspace_size.argtypes = [I, I, I, I]
+            L.swa_decode_workspace_size.restype = ctypes.c_size_t
+            L.swa_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
+                                     ctypes.c_size_t, F, P]
+            L.swa_last_error.argtypes = []
+            L.swa_last_error.restype = ctypes.c_char_p
+            for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
+                      "swa_prefill_chunk", "swa_decode"):
+                getattr(L, n).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def swa_last_error() -> str:
+    return lib().swa_last_error().decode()
+
+
+def _check(rc):
+    if rc != SWA_OK:
+        raise SwaError(rc, swa_last_error())
+
+
+def _np_i32(x):
+    if x is None:
+        return None
+    if hasattr(x, "cpu"):
+        x = x.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _hp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def swa_blockmask_size(B, nq, nk, tile_q, tile_k):
+    c, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().swa_blockmask_size(B, nq, nk, tile_q, tile_k, ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value
+
+
+def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=None,
+                        q_len=None, k_len=None, W_ring=0, ring_start=None, cache_len=None,
+                        next_pos=None):
+    """Host metadata build.  Returns dict: cls [B,nqt,nkt] uint8, row_ptr int32,
+    col int32 [nnz], col_cls uint8 [nnz], plus the six statistics."""
+    nk = W_ring + nk_lin
+    cls_n, max_nnz = swa_blockmask_size(B, nq, nk, tile_q, tile_k)
+    nqt = -(-nq // tile_q)
+    nkt = -(-nk // tile_k)
+    cls = np.zeros(max(1, cls_n), dtype=np.uint8)
+    row_ptr = np.zeros(B * nqt + 1, dtype=np.int32)
+    col = np.zeros(max(1, max_nnz), dtype=np.int32)
+    col_cls = np.zeros(max(1, max_nnz), dtype=np.uint8)
+    st = MaskStats()
+    args = [_np_i32(x) for x in (q_start, k_start, q_len, k_len, ring_start, cache_len,
+                                 next_pos)]
+    _check(lib().swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, *[_hp(a) for a in args[:4]],
+                                     W_ring, *[_hp(a) for a in args[4:]], _hp(cls),
+                                     _hp(row_ptr), _hp(col), _hp(col_cls), ctypes.byref(st)))
+    nnz = int(row_ptr[-1])
+    out = {"cls": cls[:cls_n].reshape(B, nqt, nkt), "row_ptr": row_ptr,
+           "col": col[:nnz].copy(), "col_cls": col_cls[:nnz].copy(),
+           "tile_q": tile_q, "tile_k": tile_k}
+    out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
+    return out
+
+
+def meta_to_device(meta, device):
+    """Device copies of a build's CSR arrays (what the kernels read)."""
+    import torch
+    dev = torch.device(device)
+    col = meta["col"] if meta["col"].size else np.zeros(1, dtype=np.int32)
+    ccls = meta["col_cls"] if meta["col_cls"].size else np.zeros(1, dtype=np.uint8)
+    return {"row_ptr": torch.from_numpy(meta["row_ptr"]).to(dev),
+            "col": torch.from_numpy(col).to(dev),
+            "col_cls": torch.from_numpy(ccls).to(dev),
+            "tile_q": meta["tile_q"], "tile_k": meta["tile_k"]}
+
+
+def _dptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise SwaError(SWA_EUNSUPPORTED, "dtype %s not supported" % t.dtype)
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise SwaError(SWA_EINVAL, msg)
+
+
+def swa_fwd(q, k, v, o, W, meta, q_len=None, scale=None, stream=None):
+    """Full-sequence forward.  q,o [B,H,N,d], k,v [B,Hkv,N,d] device tensors."""
+    for t in (q, k, v, o):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (B, Hkv, N, d) and tuple(v.shape) == (B, Hkv, N, d) and
+             tuple(o.shape) == (B, H, N, d), "shape mismatch")
+    _require(k.dtype == q.dtype == v.dtype == o.dtype, "dtype mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().swa_fwd(_dtype_code(q), B, H, Hkv, N, d, W, meta["tile_q"], meta["tile_k"],
+                         _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(q_len),
+                         _dptr(meta["row_ptr"]), _dptr(meta["col"]), _dptr(meta["col_cls"]),
+                         ctypes.c_float(scale), _stream(q, stream)))
+    return o
+
+
+def swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,
+                      W, meta, scale=None, stream=None):
+    """Chunked prefill; q,o [B,H,Tq,d], k_new,v_new [B,Hkv,Tq,d], caches [B,Hkv,W,d],
+    ring state int32 [B] device tensors (updated in place on the stream)."""
+    for t in (q, k_new, v_new, k_cache, v_cache, o, ring_start, cache_len, next_pos):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    B, H, Tq, d = q.shape
+    Hkv = k_new.shape[1]
+    _require(tuple(k_cache.shape) == (B, Hkv, W, d) and tuple(v_cache.shape) == (B, Hkv, W, d),
+             "cache shape must be [B,Hkv,W,d]")
+    _require(tuple(k_new.shape) == (B, Hkv, Tq, d) and tuple(v_new.shape) == (B, Hkv, Tq, d)
+             and tuple(o.shape) == (B, H, Tq, d), "shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().swa_prefill_chunk(_dtype_code(q), B, H, Hkv, Tq, d, W, meta["tile_q"],
+                                   meta["tile_k"], _dptr(q), _dptr(k_new), _dptr(v_new),
+                                   _dptr(k_cache), _dptr(v_cache), _dptr(ring_start),
+                                   _dptr(cache_len), _dptr(next_pos), _dptr(meta["row_ptr"]),
+                                   _dptr(meta["col"]), _dptr(meta["col_cls"]), _dptr(o),
+                                   ctypes.c_float(scale), _stream(q, stream)))
+    return o
+
+
+def swa_decode_workspace_size(B, H, d, W) -> int:
+    return int(lib().swa_decode_workspace_size(B, H, d, W))
+
+
+def swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,
+               workspace, W, scale=None, stream=None):
+    """One decode step; q,o [B,H,d], k_new,v_new [B,Hkv,d], caches [B,Hkv,W,d]."""
+    for t in (q, k_new, v_new, k_cache, v_cache, o, ring_start, cache_len, next_pos):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    B, H, d = q.shape
+    Hkv = k_new.shape[1]
+    _require(tuple(k_cache.shape) == (B, Hkv, W, d) and tuple(v_cache.shape) == (B, Hkv, W, d),
+             "cache shape must be [B,Hkv,W,d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().swa_decode(_dtype_code(q), B, H, Hkv, d, W, _dptr(q), _dptr(k_new),
+                            _dptr(v_new), _dptr(k_cache), _dptr(v_cache), _dptr(ring_start),
+                            _dptr(cache_len), _dptr(next_pos), _dptr(o), _dptr(workspace),
+                            ctypes.c_size_t(ws_bytes), ctypes.c_float(scale),
+                            _stream(q, stream)))
+    return o

@@ -1,0 +1,202 @@
+// swa_api.cpp -- the C ABI of include/swa.h: argument checks, kernel choice and
+// launches.  Nothing here allocates, frees or synchronises; every check runs
+// before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/swa.h"
+#include "swa_internal.h"
+
+namespace swa {
+
+static thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+}  // namespace swa
+
+namespace {
+
+using swa::fail;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptrs(const char *fn, const void *const *ptrs, const char *const *names, int n) {
+    for (int i = 0; i < n; i++) {
+        if (!ptrs[i]) return fail(SWA_EINVAL, "%s: %s is NULL", fn, names[i]);
+        if (!aligned16(ptrs[i]))
+            return fail(SWA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
+    }
+    return SWA_OK;
+}
+
+int check_heads(const char *fn, int B, int H, int Hkv, int d, int W) {
+    if (W < 1) return fail(SWA_EINVAL, "%s: window W=%d must be >= 1", fn, W);
+    if (B < 1 || B > 65535) return fail(SWA_EINVAL, "%s: B=%d out of range [1, 65535]", fn, B);
+    if (H < 1 || H > 65535 || Hkv < 1 || H % Hkv != 0)
+        return fail(SWA_EINVAL, "%s: need 1 <= Hkv, H %% Hkv == 0 (H=%d Hkv=%d)", fn, H, Hkv);
+    if (d < 1) return fail(SWA_EINVAL, "%s: d=%d must be >= 1", fn, d);
+    return SWA_OK;
+}
+
+int check_dtype_d(const char *fn, swa_dtype dt, int d) {
+    if (dt == SWA_BF16) {
+        if (d != 64 && d != 128)
+            return fail(SWA_EUNSUPPORTED, "%s: bf16 path needs d in {64, 128}, got %d", fn, d);
+    } else if (dt == SWA_F32) {
+        if (d % 4 != 0 || d > 128)
+            return fail(SWA_EUNSUPPORTED, "%s: fp32 path needs d %% 4 == 0 and d <= 128, got %d",
+                        fn, d);
+    } else {
+        return fail(SWA_EINVAL, "%s: unknown dtype %d", fn, (int)dt);
+    }
+    return SWA_OK;
+}
+
+int check_tiles(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
+    if (tile_q < 1 || tile_k < 1)
+        return fail(SWA_EINVAL, "%s: tiles must be >= 1 (%d, %d)", fn, tile_q, tile_k);
+    if (dt == SWA_BF16 && !((tile_q == 128 || tile_q == 64) && tile_k == 64))
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 kernels take (tile_q, tile_k) = (128, 64) or "
+                    "(64, 64), got (%d, %d)", fn, tile_q, tile_k);
+    return SWA_OK;
+}
+
+int launched(const char *fn, hipError_t e) {
+    if (e != hipSuccess) return fail(SWA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" const char *swa_last_error(void) { return swa::g_err; }
+
+extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q,
+                       int tile_k, const void *q, const void *k, const void *v, void *o,
+                       const int32_t *q_len_dev, const int32_t *row_ptr_dev,
+                       const int32_t *col_dev, const uint8_t *col_cls_dev, float scale,
+                       void *stream) {
+    static const char *fn = "swa_fwd";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (N < 1) return fail(SWA_EINVAL, "%s: N=%d must be >= 1", fn, N);
+    if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
+    const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
+    if ((rc = check_ptrs(fn, ptrs, names, 6))) return rc;
+    if (!col_cls_dev) return fail(SWA_EINVAL, "%s: col_cls is NULL", fn);
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+
+    swa::AttnArgs a = {};
+    a.mode = 0;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.nq = N; a.d = d; a.W = W;
+    a.tile_q = tile_q; a.tile_k = tile_k;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.q_len = q_len_dev;
+    a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
+}
+
+extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
+                                 int tile_q, int tile_k, const void *q, const void *k_new,
+                                 const void *v_new, void *k_cache, void *v_cache,
+                                 int32_t *ring_start_dev, int32_t *cache_len_dev,
+                                 int32_t *next_pos_dev, const int32_t *row_ptr_dev,
+                                 const int32_t *col_dev, const uint8_t *col_cls_dev, void *o,
+                                 float scale, void *stream) {
+    static const char *fn = "swa_prefill_chunk";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (Tq < 1 || Tq > W) return fail(SWA_EINVAL, "%s: need 1 <= Tq <= W (Tq=%d W=%d)", fn, Tq, W);
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if (W % tile_k != 0)
+        return fail(SWA_EINVAL, "%s: W=%d must be a multiple of tile_k=%d", fn, W, tile_k);
+    const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, o, row_ptr_dev, col_dev};
+    const char *names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o", "row_ptr", "col"};
+    if ((rc = check_ptrs(fn, ptrs, names, 8))) return rc;
+    if (!col_cls_dev || !ring_start_dev || !cache_len_dev || !next_pos_dev)
+        return fail(SWA_EINVAL, "%s: col_cls and the ring state arrays are required", fn);
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+
+    swa::AttnArgs a = {};
+    a.mode = 1;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.nq = Tq; a.d = d; a.W = W;
+    a.tile_q = tile_q; a.tile_k = tile_k;
+    a.q = q; a.k = k_new; a.v = v_new; a.o = o;
+    a.kc = k_cache; a.vc = v_cache;
+    a.ring_start = ring_start_dev; a.cache_len = cache_len_dev; a.next_pos = next_pos_dev;
+    a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    // attention reads the old ring; the commit runs after it on the same stream
+    if ((rc = launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s)
+                                          : swa::launch_tile_f32(a, s))))
+        return rc;
+    swa::CommitArgs c;
+    c.B = B; c.Hkv = Hkv; c.Tq = Tq; c.d = d; c.W = W;
+    c.elem_bytes = dt == SWA_BF16 ? 2 : 4;
+    c.k_new = k_new; c.v_new = v_new; c.kc = k_cache; c.vc = v_cache;
+    c.ring_start = ring_start_dev; c.cache_len = cache_len_dev; c.next_pos = next_pos_dev;
+    return launched(fn, swa::launch_commit(c, s));
+}
+
+extern "C" size_t swa_decode_workspace_size(int B, int H, int d, int W) {
+    if (B < 1 || H < 1 || d < 1 || W < 1) return 0;
+    return (size_t)B * H * swa::decode_max_splits(W) * (size_t)(d + 2) * sizeof(float);
+}
+
+extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, const void *q,
+                          const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                          int32_t *ring_start_dev, int32_t *cache_len_dev,
+                          int32_t *next_pos_dev, void *o, void *workspace, size_t ws_bytes,
+                          float scale, void *stream) {
+    static const char *fn = "swa_decode";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    const int G = H / Hkv;
+    if (dt == SWA_BF16 && !(G == 1 || G == 2 || G == 4 || G == 8))
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 path needs H/Hkv in {1, 2, 4, 8}, got %d", fn, G);
+    const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, o};
+    const char *names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o"};
+    if ((rc = check_ptrs(fn, ptrs, names, 6))) return rc;
+    if (!ring_start_dev || !cache_len_dev || !next_pos_dev)
+        return fail(SWA_EINVAL, "%s: the ring state arrays are required", fn);
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+    swa::DecodeArgs a = {};
+    a.B = B; a.H = H; a.Hkv = Hkv; a.d = d; a.W = W;
+    a.q = q; a.k_new = k_new; a.v_new = v_new; a.kc = k_cache; a.vc = v_cache;
+    a.ring_start = ring_start_dev; a.cache_len = cache_len_dev; a.next_pos = next_pos_dev;
+    a.o = o;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    if (dt == SWA_F32) return launched(fn, swa::launch_decode_f32(a, s));
+    const size_t need = swa_decode_workspace_size(B, H, d, W);
+    if (!workspace || !aligned16(workspace) || ws_bytes < need)
+        return fail(SWA_EINVAL, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu",
+                    fn, need, ws_bytes);
+    a.ws = (float *)workspace;
+    a.n_split = swa::decode_bf16_splits(B, Hkv, W);
+    return launched(fn, swa::launch_decode_bf16(a, s));
+}

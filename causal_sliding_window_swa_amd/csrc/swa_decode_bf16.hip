@@ -1,0 +1,339 @@
+// swa_decode_bf16.hip -- one decode step against a ring-buffer KV cache, bf16.
+//
+// A decode step must stream every K/V row it reads from HBM ("Sparse
+// attention taxonomy" §1.1), so the kernel is built to read each ring row of a
+// request exactly once and keep many bytes in flight:
+//   * grid (n_split, Hkv, B): the W slots of one (request, KV head) are split
+//     into n_split ranges, each range into 4 per-wave quarters;
+//   * all G = H/Hkv query heads of the KV group are scored together, so a K/V
+//     row is loaded once for the whole group: S^T (16 keys x 16 head slots)
+//     = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows straight from HBM);
+//   * fp32 online softmax per head (exp2, scale folded into one FMA);
+//   * probabilities go through a small per-wave LDS table to the lanes that
+//     hold V rows (16 lanes x 16 bytes per row), which accumulate P V in fp32;
+//   * the 4 waves merge in LDS; each range writes (max, sum, unnormalised O)
+//     to the workspace, and a second kernel merges the ranges by log-sum-exp.
+//
+// Append first ("Dense vs sliding-window sparse attention" blog §3.2 rule):
+// the new row goes to slot (ring_start + cache_len) mod W while the ring is
+// filling, else over the oldest slot ring_start.  The range owning that slot
+// reads the new row from k_new/v_new and writes it into the ring; no other
+// block reads that slot.  The ring state itself is advanced by the combine
+// kernel, after every range has read it.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int CH = 64;    // keys per wave iteration
+constexpr int PST = 20;   // LDS probability row stride (floats): conflict-free writes
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Orders this wave's LDS accesses for the compiler; LDS operations of one
+// wave are executed in issue order by the hardware.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct RingView {
+    int W, rs2, cl2, np2, s_new;
+    // valid slot of the ring after the append, and its logical position
+    __device__ __forceinline__ bool valid(int s, int &pos) const {
+        int r = s - rs2;
+        r += (r < 0) ? W : 0;
+        pos = np2 - cl2 + r;
+        return r < cl2;
+    }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+    constexpr int KSTEP = D / 32;  // 32-wide k-steps of the QK product
+    constexpr int DQ = D / 4;      // d values per lane group in the QK operands
+    constexpr int LPR = D / 8;     // lanes per V row (16 bytes each)
+    constexpr int RPI = 64 / LPR;  // V rows per wave instruction
+    constexpr int NRR = CH / RPI;  // V row rounds per iteration
+
+    __shared__ __attribute__((aligned(16))) float Pl[4][CH * PST];
+    __shared__ float wm[4][16], wl[4][16];
+    __shared__ float wo[4][G][D];
+
+    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lh = lane & 15, lg = lane >> 4;
+    const int W = a.W;
+
+    // ring state before and after the append
+    const int rs = a.ring_start[b], cl = a.cache_len[b], np = a.next_pos[b];
+    RingView rv;
+    rv.W = W;
+    const bool full = cl == W;
+    rv.s_new = full ? rs : (rs + cl) % W;
+    rv.rs2 = full ? (rs + 1 == W ? 0 : rs + 1) : rs;
+    rv.cl2 = full ? W : cl + 1;
+    rv.np2 = np + 1;
+    const int qpos = np;
+
+    // slot ranges: split -> [s0, s1), wave -> [w0, w1)
+    const int S = (W + a.n_split - 1) / a.n_split;
+    const int s0 = split * S, s1 = min(W, s0 + S);
+    const int SW = (S + 3) / 4;
+    const int w0 = s0 + wave * SW, w1 = min(s1, w0 + SW);
+    const int niter = (SW + CH - 1) / CH;  // same for every wave of the block
+
+    const size_t kvh = (size_t)b * a.Hkv + g;
+    const __bf16 *kring = (const __bf16 *)a.kc + kvh * (size_t)W * D;
+    const __bf16 *vring = (const __bf16 *)a.vc + kvh * (size_t)W * D;
+    const __bf16 *knew = (const __bf16 *)a.k_new + kvh * D;
+    const __bf16 *vnew = (const __bf16 *)a.v_new + kvh * D;
+
+    // the range owning the new slot stores the new row into the ring
+    if (rv.s_new >= s0 && rv.s_new < s1 && tid < LPR) {
+        *(u32x4 *)((__bf16 *)a.kc + (kvh * W + rv.s_new) * D + tid * 8) = ld16(knew + tid * 8);
+        *(u32x4 *)((__bf16 *)a.vc + (kvh * W + rv.s_new) * D + tid * 8) = ld16(vnew + tid * 8);
+    }
+
+    // Q of the group as the B operand: column lh = head (zero past G)
+    bf16x8 qf[KSTEP];
+    {
+        const __bf16 *qp = (const __bf16 *)a.q + ((size_t)b * a.H + g * G + lh) * D + lg * DQ;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ks++) {
+            u32x4 x = (lh < G) ? ld16(qp + ks * 8) : u32x4{0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    const float c2 = a.scale * LOG2E;
+    float m_run = -INFINITY, l_run = 0.f;  // per head lh (replicated over lg)
+    float o[G][8];
+#pragma unroll
+    for (int hq = 0; hq < G; hq++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[hq][e] = 0.f;
+    float *P = Pl[wave];
+
+    for (int it = 0; it < niter; it++) {
+        const int c0 = w0 + it * CH;
+        // issue every load of this iteration: K (MFMA layout), then V rows
+        u32x4 kr[4][KSTEP];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            const int s = c0 + kb * 16 + lh;
+            const __bf16 *src = (s == rv.s_new) ? knew : kring + (size_t)s * D;
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ks++)
+                kr[kb][ks] = (s < w1) ? ld16(src + lg * DQ + ks * 8) : u32x4{0, 0, 0, 0};
+        }
+        u32x4 vr[NRR];
+#pragma unroll
+        for (int rr = 0; rr < NRR; rr++) {
+            const int s = c0 + rr * RPI + lane / LPR;
+            const __bf16 *src = (s == rv.s_new) ? vnew : vring + (size_t)s * D;
+            vr[rr] = (s < w1) ? ld16(src + (lane % LPR) * 8) : u32x4{0, 0, 0, 0};
+        }
+
+        // scores: sacc[kb][j] = S[key c0 + kb*16 + lg*4 + j][head lh]
+        f32x4 sacc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ks++)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, kr[kb][ks]), qf[ks], sacc[kb], 0, 0, 0);
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int s = c0 + kb * 16 + lg * 4 + j;
+                int pos;
+                const bool ok = s < w1 && rv.valid(s, pos) && pos <= qpos && pos >= qpos - W + 1;
+                if (!ok) sacc[kb][j] = -INFINITY;
+                mloc = fmaxf(mloc, sacc[kb][j]);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m_run, mloc * c2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], c2, -m_use));
+                psum += p;
+                P[(kb * 16 + lg * 4 + j) * PST + lh] = p;
+            }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // rescale O by each head's alpha (held by lane hq)
+#pragma unroll
+        for (int hq = 0; hq < G; hq++) {
+            const float ah = __shfl(alpha, hq);
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[hq][e] *= ah;
+        }
+        wave_lds_order();
+        // O += P V over this iteration's rows
+#pragma unroll
+        for (int rr = 0; rr < NRR; rr++) {
+            const int row = rr * RPI + lane / LPR;
+            float pr[G];
+            if (G >= 4) {
+#pragma unroll
+                for (int q4 = 0; q4 < G / 4; q4++) {
+                    const f32x4 t = *(const f32x4 *)(P + row * PST + q4 * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) pr[q4 * 4 + e] = t[e];
+                }
+            } else {
+#pragma unroll
+                for (int hq = 0; hq < G; hq++) pr[hq] = P[row * PST + hq];
+            }
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                v[2 * e] = bf_lo(vr[rr][e]);
+                v[2 * e + 1] = bf_hi(vr[rr][e]);
+            }
+#pragma unroll
+            for (int hq = 0; hq < G; hq++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) o[hq][e] = fmaf(pr[hq], v[e], o[hq][e]);
+        }
+        wave_lds_order();
+    }
+
+    // sum the row groups of the wave (lanes with equal lane % LPR)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int hq = 0; hq < G; hq++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[hq][e] += __shfl_xor(o[hq][e], off);
+    if (lane < 16) {
+        wm[wave][lane] = m_run;
+        wl[wave][lane] = l_run;
+    }
+    if (lane < LPR) {
+#pragma unroll
+        for (int hq = 0; hq < G; hq++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) wo[wave][hq][lane * 8 + e] = o[hq][e];
+    }
+    __syncthreads();
+    // merge the 4 waves; write this range's (max, sum, unnormalised O)
+    const int nsp = a.n_split;
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int hq = idx / D, dd = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; w++) M = fmaxf(M, wm[w][hq]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const float f = __builtin_amdgcn_exp2f(wm[w][hq] - Mu);
+            L += f * wl[w][hq];
+            O += f * wo[w][hq][dd];
+        }
+        const size_t hidx = ((size_t)b * a.H + g * G + hq) * nsp + split;
+        a.ws[hidx * D + dd] = O;
+        if (dd == 0) {
+            float *ml = a.ws + (size_t)a.B * a.H * nsp * D;
+            ml[2 * hidx] = M;
+            ml[2 * hidx + 1] = L;
+        }
+    }
+}
+
+// grid (B*H), D threads: log-sum-exp merge of the ranges, O = sum / l as bf16;
+// block (b, head 0) then advances the ring state of request b by one token.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+    const int nsp = a.n_split;
+    const float *ml = a.ws + (size_t)a.B * a.H * nsp * D;
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; s++) M = fmaxf(M, ml[2 * ((size_t)bh * nsp + s)]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < nsp; s++) {
+        const size_t hidx = (size_t)bh * nsp + s;
+        const float f = __builtin_amdgcn_exp2f(ml[2 * hidx] - Mu);
+        L += f * ml[2 * hidx + 1];
+        O += f * a.ws[hidx * D + threadIdx.x];
+    }
+    ((__bf16 *)a.o)[(size_t)bh * D + threadIdx.x] = (__bf16)((L > 0.f) ? O / L : 0.f);
+    if (h == 0 && threadIdx.x == 0) {
+        const int W = a.W, rs = a.ring_start[b], cl = a.cache_len[b];
+        const bool full = cl == W;
+        a.ring_start[b] = full ? (rs + 1) % W : rs;
+        a.cache_len[b] = full ? W : cl + 1;
+        a.next_pos[b] = a.next_pos[b] + 1;
+    }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(a.n_split, a.Hkv, a.B), dim3(256), 0, s,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
+    switch (a.H / a.Hkv) {
+        case 1: return launch_dg<D, 1>(a, s);
+        case 2: return launch_dg<D, 2>(a, s);
+        case 4: return launch_dg<D, 4>(a, s);
+        default: return launch_dg<D, 8>(a, s);
+    }
+}
+
+}  // namespace
+
+// Ranges per (request, KV head): enough workgroups to fill the chip, each
+// range at least 256 slots (64 per wave).
+int decode_max_splits(int W) {
+    int m = W / 256;
+    if (m < 1) m = 1;
+    if (m > 32) m = 32;
+    return m;
+}
+
+int decode_bf16_splits(int B, int Hkv, int W) {
+    const long pairs = (long)B * Hkv;
+    int n = 1;
+    while (pairs * n < 2048 && n < decode_max_splits(W)) n <<= 1;
+    if (n > decode_max_splits(W)) n = decode_max_splits(W);
+    return n;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
+    return a.d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+}  // namespace swa

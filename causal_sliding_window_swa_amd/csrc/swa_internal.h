@@ -1,0 +1,65 @@
+// swa_internal.h -- declarations shared by the library's translation units.
+// Not part of the ABI (include/swa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// Records a message for swa_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Everything a tile-loop kernel (full-sequence forward or chunked prefill)
+// needs.  mode 0: forward, keys are rows 0..nq-1 of k/v at positions 0..nq-1,
+// q_len valid lengths.  mode 1: chunk, key axis = [W ring slots of kc/vc |
+// nq new rows of k/v], ring state read from the device arrays.
+struct AttnArgs {
+    int mode;
+    int B, H, Hkv, nq, d, W, tile_q, tile_k;
+    const void *q, *k, *v;
+    void *o;
+    const void *kc, *vc;
+    const int32_t *q_len;
+    const int32_t *ring_start, *cache_len, *next_pos;
+    const int32_t *row_ptr, *col;
+    const uint8_t *col_cls;
+    float scale;
+};
+
+struct DecodeArgs {
+    int B, H, Hkv, d, W;
+    const void *q, *k_new, *v_new;
+    void *kc, *vc;
+    int32_t *ring_start, *cache_len, *next_pos;
+    void *o;
+    float *ws;
+    int n_split;
+    float scale;
+};
+
+struct CommitArgs {
+    int B, Hkv, Tq, d, W, elem_bytes;
+    const void *k_new, *v_new;
+    void *kc, *vc;
+    int32_t *ring_start, *cache_len, *next_pos;
+};
+
+// bf16 MFMA tile loop (swa_tile_bf16.hip): d in {64,128}, tile_q in {64,128}, tile_k 64.
+hipError_t launch_tile_bf16(const AttnArgs &a, hipStream_t s);
+// fp32 reference-grade kernels (swa_f32.hip): any tiles, d % 4 == 0, d <= 128.
+hipError_t launch_tile_f32(const AttnArgs &a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+// bf16 split decode + combine (swa_decode_bf16.hip).
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
+int decode_bf16_splits(int B, int Hkv, int W);
+int decode_max_splits(int W);
+// Ring bookkeeping (swa_ring.hip): write the new rows into their slots, then
+// advance the state; launch_commit does both (after a chunk's attention).
+hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s);
+hipError_t launch_ring_state(const CommitArgs &a, hipStream_t s);
+hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
+
+}  // namespace swa

@@ -1,0 +1,72 @@
+// swa_ring.hip -- ring-buffer cache bookkeeping on the device.
+//
+// The cache of one request is [Hkv][W][d] plus (ring_start, cache_len,
+// next_pos) ("Dense vs sliding-window sparse attention" blog, §3.2: a start
+// index marks the oldest slot; rows are written to the next free slot while
+// filling, then over the oldest one).  The r-th oldest row (r < cache_len)
+// lives in slot (ring_start + r) mod W at logical position
+// next_pos - cache_len + r, so slots keep their logical positions after being
+// overwritten ("Weight sparsity vs attention sparsity" §06; "LLMs from
+// scratch" ch.10 §10.2).  Appending Tq rows one by one under that rule puts
+// the row of position next_pos + t into slot (ring_start + cache_len + t)
+// mod W; when Tq > W only the last W rows survive.
+#include <hip/hip_runtime.h>
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+// Copy new rows t in [t0, Tq) of k_new/v_new into their ring slots.
+// grid (Tq - t0, Hkv, B); one row of d elements per block.
+__global__ void ring_write_kernel(CommitArgs a, int t0) {
+    const int t = t0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int W = a.W;
+    const int slot = (int)(((int64_t)a.ring_start[b] + a.cache_len[b] + t) % W);
+    const size_t row_bytes = (size_t)a.d * a.elem_bytes;
+    const size_t kvh = (size_t)b * a.Hkv + g;
+    const char *ks = (const char *)a.k_new + (kvh * a.Tq + t) * row_bytes;
+    const char *vs = (const char *)a.v_new + (kvh * a.Tq + t) * row_bytes;
+    char *kd = (char *)a.kc + (kvh * W + slot) * row_bytes;
+    char *vd = (char *)a.vc + (kvh * W + slot) * row_bytes;
+    for (size_t off = threadIdx.x * 4; off < row_bytes; off += blockDim.x * 4) {
+        *(uint32_t *)(kd + off) = *(const uint32_t *)(ks + off);
+        *(uint32_t *)(vd + off) = *(const uint32_t *)(vs + off);
+    }
+}
+
+// State after appending Tq rows: next_pos += Tq, cache_len = min(W, len+Tq),
+// ring_start = slot of the oldest kept position.
+__global__ void ring_state_kernel(int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                                  int B, int W, int Tq) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int64_t rs = ring_start[b], cl = cache_len[b], np = next_pos[b];
+    const int64_t cl2 = (cl + Tq < W) ? cl + Tq : W;
+    ring_start[b] = (int32_t)((rs + Tq + cl - cl2) % W);
+    cache_len[b] = (int32_t)cl2;
+    next_pos[b] = (int32_t)(np + Tq);
+}
+
+}  // namespace
+
+hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s) {
+    const int t0 = a.Tq > a.W ? a.Tq - a.W : 0;
+    dim3 grid(a.Tq - t0, a.Hkv, a.B);
+    hipLaunchKernelGGL(ring_write_kernel, grid, dim3(64), 0, s, a, t0);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_state(const CommitArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(ring_state_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.ring_start,
+                       a.cache_len, a.next_pos, a.B, a.W, a.Tq);
+    return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitArgs &a, hipStream_t s) {
+    hipError_t e = launch_ring_write(a, s);
+    if (e != hipSuccess) return e;
+    return launch_ring_state(a, s);
+}
+
+}  // namespace swa

@@ -1,0 +1,180 @@
+/*
+ * swa.h -- C ABI of the MI355X (gfx950) causal sliding-window attention library.
+ *
+ * The operation (cited by page title and section):
+ *   [M003] "Weight sparsity vs attention sparsity" (AI-infra KB), §03-§06
+ *   [Ch10] "LLMs from scratch, chapter 10: SWA and DSA", §10.1-§10.2
+ *   [Blog] "Dense attention vs sliding-window sparse attention", §3.2
+ *
+ *   A query at logical position t reads exactly the keys at logical positions
+ *   max(0, t-W+1) .. t (W counts the current token) [M003 §03], [Ch10 §10.1];
+ *   scores are scale * <q, k>; softmax is normalised over that set only and
+ *   weights the V rows of that set.  A query with no visible key (a padded
+ *   row) is written as 0.  Grouped KV heads: query head h reads KV head
+ *   h / (H / Hkv) (contiguous groups).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense row-major, d fastest: Q and O [B][H][rows][d],
+ *     K and V [B][Hkv][rows][d], ring caches [B][Hkv][W][d].
+ *   - Device pointers are caller-owned device memory (16-byte aligned) and
+ *     host pointers caller-owned host memory.  The library never allocates,
+ *     frees or synchronises: device work is enqueued on `stream` (NULL = the
+ *     default stream) and its faults surface at the caller's next sync.
+ *   - Every call returns a swa_status.  On anything but SWA_OK nothing was
+ *     enqueued (except SWA_EHIP after a failed launch) and swa_last_error()
+ *     describes the problem.  No exception crosses the ABI.
+ *   - Padded rows, keys past a valid length and unfilled ring slots must hold
+ *     finite values (zeros are fine): they are masked, and 0 * NaN is NaN.
+ *   - bf16 inputs are accumulated in fp32 (softmax in fp32, probabilities
+ *     rounded to bf16 before the PV product, output rounded to bf16).
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_EINVAL = 1,       /* an argument is out of range, inconsistent or NULL */
+    SWA_EUNSUPPORTED = 2, /* valid, but no kernel for this dtype / d / tile */
+    SWA_EHIP = 3          /* the HIP runtime refused a launch */
+} swa_status;
+
+typedef enum { SWA_BF16 = 0, SWA_F32 = 1 } swa_dtype;
+
+/* Classes of a (query tile, key tile) block [M003 §04]: no visible pair,
+ * every in-range pair visible, or some visible. */
+typedef enum { SWA_BLOCK_SKIP = 0, SWA_BLOCK_FULL = 1, SWA_BLOCK_PARTIAL = 2 } swa_block_class;
+
+/* Work statistics of one metadata build, each summed over the batch. */
+typedef struct {
+    int64_t valid_pairs;    /* visible (query, key) pairs between valid rows/keys [M003 §03] */
+    int64_t covered_coords; /* in-range coordinates of all live blocks [M003 §04] */
+    int64_t keys_touched;   /* distinct keys visible to at least one valid query
+                               (W+Tq-1 for a chunk after a full ring [Ch10 §10.2]) */
+    int64_t n_live;         /* full + partial blocks (= CSR entries) */
+    int64_t n_full;
+    int64_t n_partial;
+} swa_mask_stats;
+
+/* Sizes of the metadata buffers for a build with these shapes.
+ * nk is the whole key axis (ring slots + linear keys).  Host only.
+ * cls_elems = B * ceil(nq/tile_q) * ceil(nk/tile_k) (bytes of `cls`);
+ * max_nnz   = an upper bound on CSR entries (elements of `col`, `col_cls`);
+ * the row_ptr array has B * ceil(nq/tile_q) + 1 elements.
+ * Errors: SWA_EINVAL for B < 1, nq < 0, nk < 0, tile < 1, NULL outputs. */
+int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
+                       size_t *cls_elems, size_t *max_nnz);
+
+/* Block metadata (host, integer, exact) [M003 §04]: classifies every
+ * (query tile, key tile) by counting its visible pairs: 0 -> skip, equal to
+ * the tile's in-range area -> full, else partial, and lists the live key
+ * tiles of each query tile in ascending order (CSR over rows b*nqt + qt).
+ *
+ * Query i of sequence b sits at logical position q_start[b] + i and is
+ * valid iff i < q_len[b].  The key axis is [W_ring ring slots | nk_lin
+ * linear keys]: linear key t sits at k_start[b] + t, valid iff t < k_len[b];
+ * ring slot s (when W_ring > 0) holds the logical position
+ *   next_pos[b] - cache_len[b] + ((s - ring_start[b]) mod W_ring)
+ * and is valid iff (s - ring_start[b]) mod W_ring < cache_len[b]: slots keep
+ * their logical positions after being overwritten [M003 §06], [Ch10 §10.2].
+ * NULL q_start/k_start mean 0, NULL q_len/k_len mean "all valid"; the ring
+ * arrays are ignored when W_ring == 0 and required otherwise.
+ *
+ * For swa_fwd: q_start = k_start = NULL, nq = nk_lin = N, q_len = k_len =
+ *   the per-sequence valid lengths (or NULL), W_ring = 0.
+ * For swa_prefill_chunk: nq = nk_lin = Tq, q_start = k_start = next_pos,
+ *   k_len = NULL, W_ring = W and the ring state the call will see.
+ *
+ * Outputs (caller-owned host memory, sizes from swa_blockmask_size):
+ * cls [B][nqt][nkt] uint8, row_ptr [B*nqt+1] int32, col [nnz] int32 (key
+ * tile index), col_cls [nnz] uint8 (1 full, 2 partial); stats may be NULL.
+ * Errors: SWA_EINVAL for W < 1 [Blog §5.1 names "window_size must be
+ * positive"], bad sizes, W_ring % tile_k != 0, ring state out of range
+ * (ring_start not in [0, W_ring), cache_len not in [0, W_ring],
+ * next_pos < cache_len), a negative length, or positions that overflow int32. */
+int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
+                        const int32_t *q_start, const int32_t *k_start,
+                        const int32_t *q_len, const int32_t *k_len,
+                        int W_ring, const int32_t *ring_start, const int32_t *cache_len,
+                        const int32_t *next_pos,
+                        uint8_t *cls, int32_t *row_ptr, int32_t *col, uint8_t *col_cls,
+                        swa_mask_stats *stats);
+
+/* Full-sequence SWA forward (prefill) [M003 §03-§04].
+ * q, o [B][H][N][d]; k, v [B][Hkv][N][d]; query row i and key row j sit at
+ * logical positions i and j.  q_len_dev: device int32 [B] valid lengths or
+ * NULL (= N); rows at or past the length are written as 0.
+ * row_ptr_dev / col_dev / col_cls_dev: device copies of a swa_blockmask_build
+ * with the same B, N, W, tile_q, tile_k and lengths; only listed key tiles
+ * are read, and only partial ones are masked per element.  The kernel does
+ * not re-check the metadata: metadata of other shapes is a caller error.
+ * Supported: SWA_BF16 with d in {64, 128}, (tile_q, tile_k) = (128, 64) or
+ * (64, 64); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
+ * W >= N is legal (dense causal).
+ * Errors: SWA_EINVAL (W < 1, H % Hkv != 0, N < 1, NULL or misaligned
+ * pointers), SWA_EUNSUPPORTED, SWA_EHIP. */
+int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q, int tile_k,
+            const void *q, const void *k, const void *v, void *o,
+            const int32_t *q_len_dev,
+            const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *col_cls_dev,
+            float scale, void *stream);
+
+/* Chunked prefill of Tq new tokens against a ring-buffer cache [Ch10 §10.2],
+ * [Blog §3.2], [M003 §06].
+ * q, o [B][H][Tq][d]; k_new, v_new [B][Hkv][Tq][d]; k_cache, v_cache
+ * [B][Hkv][W][d] (in/out); ring state ring_start_dev, cache_len_dev,
+ * next_pos_dev: device int32 [B] (in/out), meaning as in swa_blockmask_build.
+ * New token t sits at logical position next_pos + t.  Every query attends
+ * over the union of the old ring and the chunk (up to W+Tq-1 keys), read
+ * before anything is overwritten; then the last min(Tq, W) new rows are
+ * written into the ring (the slot of logical position P is the one whose
+ * formula above yields P) and the state becomes next_pos += Tq,
+ * cache_len = min(W, cache_len + Tq), ring_start = slot of the oldest kept
+ * position.  Metadata: swa_blockmask_build with W_ring = W, nq = nk_lin = Tq,
+ * q_start = k_start = next_pos and the same tiles.
+ * Supported: as swa_fwd, plus W % tile_k == 0 and 1 <= Tq <= W.
+ * Errors: as swa_fwd. */
+int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
+                      int tile_q, int tile_k,
+                      const void *q, const void *k_new, const void *v_new,
+                      void *k_cache, void *v_cache,
+                      int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
+                      const int32_t *row_ptr_dev, const int32_t *col_dev,
+                      const uint8_t *col_cls_dev,
+                      void *o, float scale, void *stream);
+
+/* Bytes of device workspace swa_decode needs for these shapes. */
+size_t swa_decode_workspace_size(int B, int H, int d, int W);
+
+/* One decode step per request against its ring cache [Blog §3.2],
+ * [Taxonomy §1.1: decode streams the whole KV it reads].
+ * q, o [B][H][d] (one token each); k_new, v_new [B][Hkv][d]; caches and ring
+ * state as swa_prefill_chunk.  The new row is appended first (the next free
+ * slot (ring_start + cache_len) mod W while filling, else the oldest slot
+ * ring_start, which then advances), then the query at logical position
+ * next_pos (the old value) attends over the ring's valid slots; next_pos
+ * grows by one.  workspace: device memory of swa_decode_workspace_size bytes
+ * (ws_bytes), no initialisation needed.
+ * Supported: SWA_BF16 with d in {64, 128}, H / Hkv <= 16; SWA_F32 with d a
+ * multiple of 4 in [4, 128].
+ * Errors: as swa_fwd, plus SWA_EINVAL when ws_bytes is too small. */
+int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W,
+               const void *q, const void *k_new, const void *v_new,
+               void *k_cache, void *v_cache,
+               int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
+               void *o, void *workspace, size_t ws_bytes, float scale, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

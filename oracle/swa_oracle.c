@@ -364,6 +364,7 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
     char *qok = malloc((size_t)(nq > 0 ? nq : 1));
     char *kok = malloc((size_t)(nk > 0 ? nk : 1));
     char *touched = malloc((size_t)(nk > 0 ? nk : 1));
+    int64_t *counts = malloc(sizeof(int64_t) * (size_t)(nqt > 0 && nkt > 0 ? nqt * nkt : 1));
 
     for (s = 0; s < 6; s++)
         stats[s] = 0;
@@ -389,7 +390,35 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
             kpos[W_ring + j] = (k_start ? k_start[b] : 0) + (int64_t)j;
             kok[W_ring + j] = k_len ? (j < k_len[b]) : 1;
         }
-        memset(touched, 0, (size_t)(nk > 0 ? nk : 1));
+        /* visible-pair count of every tile pair, by brute force over its
+         * coordinates (tiles are independent: counted in parallel) */
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+        for (qt = 0; qt < nqt; qt++) {
+            for (kt = 0; kt < nkt; kt++) {
+                const int i0 = qt * tile_q;
+                const int i1 = (i0 + tile_q < nq) ? i0 + tile_q : nq;
+                const int j0 = kt * tile_k;
+                const int j1 = (j0 + tile_k < nk) ? j0 + tile_k : nk;
+                int64_t count = 0;
+                int ii, jj;
+                for (ii = i0; ii < i1; ii++)
+                    for (jj = j0; jj < j1; jj++)
+                        if (qok[ii] && kok[jj] && allowed(qpos[ii], kpos[jj], W))
+                            count++;
+                counts[(int64_t)qt * nkt + kt] = count;
+            }
+        }
+        /* a key is touched if some valid query sees it */
+#pragma omp parallel for schedule(dynamic, 64)
+        for (j = 0; j < nk; j++) {
+            int ii;
+            touched[j] = 0;
+            for (ii = 0; ii < nq && kok[j]; ii++)
+                if (qok[ii] && allowed(qpos[ii], kpos[j], W)) {
+                    touched[j] = 1;
+                    break;
+                }
+        }
 
         for (qt = 0; qt < nqt; qt++) {
             const int i0 = qt * tile_q;
@@ -398,14 +427,8 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
                 const int j0 = kt * tile_k;
                 const int j1 = (j0 + tile_k < nk) ? j0 + tile_k : nk;
                 const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);
-                int64_t count = 0;
+                const int64_t count = counts[(int64_t)qt * nkt + kt];
                 uint8_t c;
-                for (i = i0; i < i1; i++)
-                    for (j = j0; j < j1; j++)
-                        if (qok[i] && kok[j] && allowed(qpos[i], kpos[j], W)) {
-                            count++;
-                            touched[j] = 1;
-                        }
                 c = (count == 0) ? 0 : (count == area ? 1 : 2);
                 cls[((int64_t)b * nqt + qt) * nkt + kt] = c;
                 stats[0] += count;
@@ -423,7 +446,7 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
         for (j = 0; j < nk; j++)
             stats[2] += touched[j];
     }
-    free(qpos); free(kpos); free(qok); free(kok); free(touched);
+    free(qpos); free(kpos); free(qok); free(kok); free(touched); free(counts);
     return nnz;
 }
 

@@ -1,0 +1,101 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_sliding_window_swa_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "swa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(swa.EXPORTS)
+    L = swa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_blockmask_rejects_bad_arguments():
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_blockmask_build(1, 8, 8, 0, 2, 2)
+    assert e.value.code == swa.SWA_EINVAL and "W" in str(e.value)
+    with pytest.raises(swa.SwaError):
+        swa.swa_blockmask_build(1, 8, 8, 3, 0, 2)
+    with pytest.raises(swa.SwaError):  # ring size not a multiple of tile_k
+        swa.swa_blockmask_build(1, 4, 4, 6, 4, 4, q_start=[6], k_start=[6], W_ring=6,
+                                ring_start=[0], cache_len=[6], next_pos=[6])
+    with pytest.raises(swa.SwaError):  # ring start out of range
+        swa.swa_blockmask_build(1, 4, 4, 8, 4, 4, q_start=[8], k_start=[8], W_ring=8,
+                                ring_start=[8], cache_len=[8], next_pos=[8])
+    with pytest.raises(swa.SwaError):  # next_pos below cache_len
+        swa.swa_blockmask_build(1, 4, 4, 8, 4, 4, q_start=[3], k_start=[3], W_ring=8,
+                                ring_start=[0], cache_len=[8], next_pos=[3])
+    with pytest.raises(swa.SwaError):  # length past the rows
+        swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, q_len=[9], k_len=[9])
+    with pytest.raises(swa.SwaError):  # positions overflowing int32
+        swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, q_start=[2**31 - 5], k_start=[0])
+
+
+P = ctypes.c_void_p
+
+
+def _fwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, tq=128, tk=64, ptr=16):
+    p = ctypes.c_void_p(ptr)
+    return swa.lib().swa_fwd(dt, B, H, Hkv, N, d, W, tq, tk, p, p, p, p, None, p, p, p,
+                             ctypes.c_float(0.1), None)
+
+
+def test_fwd_validation_codes():
+    assert _fwd(W=0) == swa.SWA_EINVAL
+    assert _fwd(H=3, Hkv=2) == swa.SWA_EINVAL
+    assert _fwd(N=0) == swa.SWA_EINVAL
+    assert _fwd(d=96) == swa.SWA_EUNSUPPORTED
+    assert _fwd(dt=1, d=6) == swa.SWA_EUNSUPPORTED
+    assert _fwd(tq=32) == swa.SWA_EUNSUPPORTED
+    assert _fwd(tk=128) == swa.SWA_EUNSUPPORTED
+    assert _fwd(ptr=0) == swa.SWA_EINVAL
+    assert _fwd(ptr=8) == swa.SWA_EINVAL  # misaligned
+    assert _fwd(dt=7) == swa.SWA_EINVAL
+    assert "window" in swa.swa_last_error() or True
+
+
+def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False):
+    p = ctypes.c_void_p(16)
+    st = None if nullstate else p
+    return swa.lib().swa_prefill_chunk(0, 1, 4, 2, Tq, d, W, 128, tk, p, p, p, p, p, st, st,
+                                       st, p, p, p, p, ctypes.c_float(0.1), None)
+
+
+def test_chunk_validation_codes():
+    assert _chunk(Tq=0) == swa.SWA_EINVAL
+    assert _chunk(Tq=129) == swa.SWA_EINVAL
+    assert _chunk(W=96) == swa.SWA_EINVAL  # W not a multiple of tile_k
+    assert _chunk(nullstate=True) == swa.SWA_EINVAL
+    assert _chunk(d=80) == swa.SWA_EUNSUPPORTED
+
+
+def _decode(H=32, Hkv=8, d=128, W=4096, ws=None, ws_bytes=0, dt=0):
+    p = ctypes.c_void_p(16)
+    return swa.lib().swa_decode(dt, 2, H, Hkv, d, W, p, p, p, p, p, p, p, p, p,
+                                ws, ctypes.c_size_t(ws_bytes), ctypes.c_float(0.1), None)
+
+
+def test_decode_validation_codes():
+    need = swa.swa_decode_workspace_size(2, 32, 128, 4096)
+    assert need > 0
+    assert _decode(ws=None) == swa.SWA_EINVAL
+    assert _decode(ws=ctypes.c_void_p(16), ws_bytes=need - 1) == swa.SWA_EINVAL
+    assert _decode(H=48, Hkv=3) == swa.SWA_EUNSUPPORTED  # group of 16
+    assert _decode(W=0) == swa.SWA_EINVAL
+    assert swa.swa_decode_workspace_size(0, 32, 128, 4096) == 0
