@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the SWA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline step is the full-sequence SWA forward on
+the prefill workload (B=1, H=Hkv=32, N=8192, W=512, d=128, bf16, tiles
+128x64), whose block metadata is built once on the host beforehand (a fixed
+pattern reuses its metadata); `value` is useful TFLOP/s = 4*d*(visible pairs)
+per step over the wall time of K steps.  The same run also measures, each on
+its own synthetic workload, the GQA prefill with per-sequence lengths, the
+chunked prefill against a ring cache and the ring decode (KV GB/s), and times
+the fp64 oracle on a bounded sample on the host cores.
+Inputs are seeded synthetic tensors already resident in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list: prefill,gqa,chunk,decode")
+    return ap.parse_args()
+
+
+def src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "causal_sliding_window_swa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(kernel_key, digest):
+    """HBM traffic per launch measured by rocprofv3 counters, if the record in
+    profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only; --gpus %d is not supported "
+                         "(the per-GPU kernels need no communication; see DESIGN.md)\n"
+                         % args.gpus)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import causal_sliding_window_swa_amd as swa
+    from causal_sliding_window_swa_amd import synth
+
+    only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode"}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    K, WU = args.steps, args.warmup
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    def timed(fn, steps, warmup, reset=None):
+        """wall ms per step over `steps` launches, and mean event-timed ms."""
+        for _ in range(warmup):
+            if reset:
+                reset()
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if reset:
+                reset()
+            fn()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for s, e in evs:
+            if reset:
+                reset()
+            s.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        ev = sum(s.elapsed_time(e) for s, e in evs) / steps
+        return wall, ev
+
+    out = {}
+
+    # ---------------- prefill workload (headline) ----------------
+    inp = synth.make("prefill")
+    B, H, N, d = inp["q"].shape
+    W, tq, tk = 512, 128, 64
+    t0 = time.perf_counter()
+    meta = swa.swa_blockmask_build(B, N, N, W, tq, tk)
+    t_meta = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    md = swa.meta_to_device(meta, dev)
+    torch.cuda.synchronize()
+    t_h2d = (time.perf_counter() - t0) * 1e3
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    flops = 4.0 * d * meta["valid_pairs"] * H
+    fwd = lambda: swa.swa_fwd(q, k, v, o, W, md)
+    wall_ms, ev_ms = timed(fwd, K, WU)
+    log("prefill: wall %.4f ms/step, event %.4f ms/launch" % (wall_ms, ev_ms))
+    # end to end with the metadata rebuilt and copied each step
+    def fwd_with_meta():
+        m = swa.swa_blockmask_build(B, N, N, W, tq, tk)
+        mdd = swa.meta_to_device(m, dev)
+        swa.swa_fwd(q, k, v, o, W, mdd)
+    e2e_ms, _ = timed(fwd_with_meta, max(5, K // 5), 2)
+    prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, flops=flops, meta_ms=t_meta,
+                   meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
+    out["prefill"] = prefill
+    del inp
+
+    # ---------------- GQA prefill with per-sequence lengths -------------
+    if "gqa" in only:
+        inp = synth.make("prefill_gqa")
+        B3, H3, N3, d3 = inp["q"].shape
+        L = inp["q_len"].numpy()
+        m3 = swa.swa_blockmask_build(B3, N3, N3, 4096, tq, tk, q_len=L, k_len=L)
+        md3 = swa.meta_to_device(m3, dev)
+        q3, k3, v3 = (inp[x].to(dev) for x in ("q", "k", "v"))
+        ql3 = inp["q_len"].to(dev)
+        o3 = torch.empty_like(q3)
+        del inp
+        f3 = lambda: swa.swa_fwd(q3, k3, v3, o3, 4096, md3, q_len=ql3)
+        w3, e3 = timed(f3, max(3, K // 10), 2)
+        out["gqa"] = dict(wall_ms=w3, kernel_ms=e3, flops=4.0 * d3 * m3["valid_pairs"] * H3)
+        log("gqa: wall %.3f ms, event %.3f ms" % (w3, e3))
+        del q3, k3, v3, o3
+
+    # ---------------- chunked prefill against the ring -------------
+    if "chunk" in only:
+        inp = synth.make("chunk")
+        B4, H4, Tq, d4 = inp["q"].shape
+        W4 = 4096
+        p = inp["next_pos"].numpy()
+        m4 = swa.swa_blockmask_build(B4, Tq, Tq, W4, tq, tk, q_start=p, k_start=p, W_ring=W4,
+                                     ring_start=inp["ring_start"].numpy(),
+                                     cache_len=inp["cache_len"].numpy(), next_pos=p)
+        md4 = swa.meta_to_device(m4, dev)
+        dv = {x: inp[x].to(dev) for x in inp}
+        state0 = {x: dv[x].clone() for x in ("ring_start", "cache_len", "next_pos")}
+        o4 = torch.empty_like(dv["q"])
+        del inp
+
+        def reset4():  # same ring state each step, so the metadata stays valid
+            for x in state0:
+                dv[x].copy_(state0[x])
+
+        f4 = lambda: swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                           dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                           dv["next_pos"], o4, W4, md4)
+        w4, e4 = timed(f4, max(5, K // 5), 2, reset=reset4)
+        out["chunk"] = dict(wall_ms=w4, kernel_ms=e4, flops=4.0 * d4 * m4["valid_pairs"] * H4,
+                            keys_touched_per_request=m4["keys_touched"] // B4)
+        log("chunk: wall %.3f ms, event %.3f ms" % (w4, e4))
+        del dv, o4
+
+    # ---------------- ring decode -------------
+    if "decode" in only:
+        inp = synth.make("decode")
+        B5, H5, d5 = inp["q"].shape
+        Hkv5 = inp["k_new"].shape[1]
+        W5 = 4096
+        dv = {x: inp[x].to(dev) for x in inp}
+        o5 = torch.empty_like(dv["q"])
+        ws = torch.empty(swa.swa_decode_workspace_size(B5, H5, d5, W5) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+        del inp
+        f5 = lambda: swa.swa_decode(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                    dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                    dv["next_pos"], o5, ws, W5)
+        w5, e5 = timed(f5, max(10, K), 5)
+        kv_bytes = 2.0 * B5 * Hkv5 * W5 * d5 * 2
+        out["decode"] = dict(wall_ms=w5, kernel_ms=e5, kv_bytes=kv_bytes)
+        log("decode: wall %.4f ms, event %.4f ms" % (w5, e5))
+        del dv
+
+    # ---------------- oracle on the host cores -------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, ROOT)
+        import oracle
+        inp = synth.make("prefill")
+        nh = 4
+        qs = inp["q"][:, :nh].float().numpy().astype(np.float64)
+        ks = inp["k"][:, :nh].float().numpy().astype(np.float64)
+        vs = inp["v"][:, :nh].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.fwd(qs, ks, vs, 512, 1 / math.sqrt(128))
+        sec = time.perf_counter() - t0
+        sample_flops = 4.0 * 128 * meta["valid_pairs"] * nh
+        cpu = {"value": sample_flops / sec / 1e12, "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "prefill workload heads 0-%d (%d of 32 heads, all 8192 rows), "
+                         "fp64, %.1f s" % (nh - 1, nh, sec)}
+        log("oracle: %.2f s for %d heads" % (sec, nh))
+
+    pf = out["prefill"]
+    value = pf["flops"] / (pf["wall_ms"] * 1e-3) / 1e12
+    achieved = pf["flops"] / (pf["kernel_ms"] * 1e-3) / 1e12
+    tile_digest = src_digest("swa_tile_bf16.hip")
+    line = {
+        "metric": "SWA prefill useful TFLOP/s + decode KV GB/s, each as % of MI355X peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": WU,
+        "ms_per_step": round(pf["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=1 H=32 Hkv=32 N=8192 W=512 d=128 bf16, "
+                               "tiles 128x64, metadata prebuilt",
+                   "global_batch": 1, "seq_len": 8192, "window": 512,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counters_for("swa_fwd_prefill", tile_digest),
+                     "kernel": "swa::tile_kernel<0,128,4> (swa_fwd)",
+                     "kernel_ms": round(pf["kernel_ms"], 5)},
+        "metadata": {"build_ms": round(pf["meta_ms"], 4), "h2d_ms": round(pf["meta_h2d_ms"], 4),
+                     "e2e_ms_per_step_with_build": round(pf["e2e_ms"], 4),
+                     "e2e_TFLOPs_with_build": round(pf["flops"] / (pf["e2e_ms"] * 1e-3) / 1e12,
+                                                    2),
+                     "valid_pairs": pf["stats"]["valid_pairs"],
+                     "live_blocks": pf["stats"]["n_live"],
+                     "covered_coords": pf["stats"]["covered_coords"]},
+        "cpu_baseline": cpu,
+    }
+    if "decode" in out:
+        dd = out["decode"]
+        gbs = dd["kv_bytes"] / (dd["wall_ms"] * 1e-3) / 1e9
+        gbs_k = dd["kv_bytes"] / (dd["kernel_ms"] * 1e-3) / 1e9
+        line["decode"] = {"workload": "decode B=64 H=32 Hkv=8 W=4096 d=128 bf16, full rings",
+                          "GB_per_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                          "ms_per_step": round(dd["wall_ms"], 5),
+                          "roofline": {"bound": "hbm", "achieved": round(gbs_k, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(gbs_k / PEAK_HBM_GBS, 4),
+                                       "traffic": counters_for(
+                                           "swa_decode", src_digest("swa_decode_bf16.hip")),
+                                       "kernel_ms": round(dd["kernel_ms"], 5),
+                                       "kernels": "split + combine"}}
+    if "gqa" in out:
+        g3 = out["gqa"]
+        t = g3["flops"] / (g3["wall_ms"] * 1e-3) / 1e12
+        line["prefill_gqa"] = {"workload": "prefill B=4 H=32 Hkv=8 N=32768 W=4096 d=128 bf16, "
+                                           "lengths U[8192,32768]",
+                               "TFLOP_per_s": round(t, 2),
+                               "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                               "ms_per_step": round(g3["wall_ms"], 4)}
+    if "chunk" in out:
+        c4 = out["chunk"]
+        t = c4["flops"] / (c4["wall_ms"] * 1e-3) / 1e12
+        line["chunk"] = {"workload": "chunked prefill B=8 H=32 Hkv=8 Tq=512 W=4096 d=128 bf16",
+                         "TFLOP_per_s": round(t, 2),
+                         "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                         "ms_per_step": round(c4["wall_ms"], 4),
+                         "keys_touched_per_request": c4["keys_touched_per_request"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

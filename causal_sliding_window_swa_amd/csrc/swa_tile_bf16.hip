@@ -9,19 +9,25 @@
 // partial tiles are masked per element.
 //
 // Work split (tile_q = 32 * NW query rows, tile_k = 64 keys, head dim D):
-//   * one workgroup per (query tile, head, batch); NW waves, 32 query rows each;
-//   * K tile staged in LDS row-major [key][d]; V tile staged transposed
-//     [d][key] so that PV operands are key-contiguous;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
-//     wave's Q rows kept in registers).  The transposed product leaves each
-//     lane with one query column, so row max / sum need one cross-half swap;
-//   * fp32 online softmax with exp2 and the scale folded into one FMA; a row
-//     whose running max is still -inf uses 0 instead (no -inf - -inf);
-//   * P rounded to bf16 feeds O^T += V^T P^T directly from the S registers
-//     (keys are permuted consistently between the two operands);
-//   * inside a partial tile a wave skips a 32-key half in which none of its
-//     32 rows sees any key (finer than the metadata, same result);
-//   * the next tile's K/V are loaded into registers while this one computes.
+//   * one workgroup per (query tile, head, batch), ordered so that each XCD
+//     walks a contiguous range of query tiles (neighbouring tiles share most
+//     of their K/V rows, which then hit in that XCD's L2);
+//   * K and V tiles go straight from HBM to LDS (global_load_lds_dwordx4, no
+//     register staging), double-buffered: the next tile streams in while this
+//     one is computed; rows are XOR-swizzled in 16-byte chunks so that both
+//     LDS read patterns below are free of bank conflicts;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows read from LDS,
+//     B = the wave's 32 query rows kept in registers.  Each lane then holds
+//     one query column, so row max and sum need one swap across wave halves;
+//   * fp32 online softmax in the exp2 domain with the scale folded into one
+//     FMA; the running max is only raised (and O rescaled) when a row's tile
+//     max exceeds it by more than 8, which keeps every exp2 argument <= 8 and
+//     the result exact; rows whose max is still -inf use 0 (no -inf - -inf);
+//   * O^T += V^T P^T: P comes straight from the S registers (rounded to bf16)
+//     and V^T from LDS with ds_read_b64_tr_b16, which transposes 4x4 blocks of
+//     16-bit values across lanes, so V stays row-major in LDS;
+//   * inside a partial tile a wave skips a 32-key half in which none of its 32
+//     rows sees any key (finer than the metadata, same result).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -32,28 +38,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int BN = 64;                 // keys per tile
+constexpr int BN = 64;  // keys per tile
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_SLACK = 8.0f;  // exp2 arguments stay <= 8 between rescales
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 
-__device__ __forceinline__ float wave_xor32_max(float x) {
-    return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
-
 // Logical position and validity of key `j` (0..BN-1) of key tile kt.
+template <int MODE>
 struct KeyPos {
-    int mode, nq, W, nrt, qlen;
-    int rs, cl;
-    int np;
+    int nq, W, nrt, qlen, rs, cl, np;
     __device__ __forceinline__ void at(int kt, int j, int &pos, bool &ok) const {
-        if (mode == 0) {
+        if (MODE == 0) {
             pos = kt * BN + j;
             ok = pos < qlen;
         } else if (kt < nrt) {
@@ -70,31 +72,38 @@ struct KeyPos {
     }
 };
 
+// Workgroup p of T runs logical tile L: XCD x = p % 8 gets the contiguous
+// logical range [start_x, start_x + count_x) in dispatch order.
+__device__ __forceinline__ int xcd_remap(int p, int T) {
+    const int x = p & 7, i = p >> 3, q = T >> 3, r = T & 7;
+    return x * q + (x < r ? x : r) + i;
+}
+
 template <int MODE, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
-    constexpr int NT = NW * 64;
-    constexpr int KS = D / 16;    // k-steps of the QK product
-    constexpr int DB = D / 32;    // 32-wide d blocks of the output
-    constexpr int DC = D / 8;     // 16-byte chunks per row
-    constexpr int KROW = D + 8;   // LDS K row stride (bf16 elements)
-    constexpr int VROW = BN + 4;  // LDS V^T row stride (bf16 elements)
-    constexpr int KLD = BN * DC / NT;        // 16-byte K loads per thread per tile
-    constexpr int VLD = (BN / 2) * DC / NT;  // (key pair, chunk) tasks per thread
-    static_assert(KLD >= 1 && VLD >= 1, "tile too small for the block");
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void tile_kernel(AttnArgs a) {
+    constexpr int KS = D / 16;          // k-steps of the QK product
+    constexpr int DB = D / 32;          // 32-wide d blocks of the output
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RPL = 64 / CPR;       // rows per wave-wide 1 KB load
+    constexpr int LPW = BN / RPL / NW;  // such loads per wave, per matrix, per tile
+    constexpr int ROWB = D * 2;         // bytes per row
+    constexpr int TILEB = BN * ROWB;    // bytes per K (or V) tile
+    static_assert(LPW >= 1, "tile too small for the block");
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * KROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VROW];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];  // [stage][K, V]
 
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 31, hh = lane >> 5;
-    const int G = a.H / a.Hkv;
-    const int g = h / G;
     const int nq = a.nq;
     const int nqt = (nq + 32 * NW - 1) / (32 * NW);
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = L % nqt, h = (L / nqt) % a.H, b = L / (nqt * a.H);
+    const int G = a.H / a.Hkv;
+    const int g = h / G;
 
-    KeyPos kp;
-    kp.mode = MODE;
+    KeyPos<MODE> kp;
     kp.nq = nq;
     kp.W = a.W;
     kp.nrt = (MODE == 1) ? a.W / BN : 0;
@@ -108,65 +117,50 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
     // ---- this wave's 32 query rows in registers (B operand of S^T = K Q^T)
     const int row0 = qt * 32 * NW + wave * 32;
     const int myrow = row0 + lq;
-    const __bf16 *qp = (const __bf16 *)a.q + (((size_t)b * a.H + h) * nq + myrow) * D;
     bf16x8 qf[KS];
+    {
+        const __bf16 *qp = (const __bf16 *)a.q + (((size_t)b * a.H + h) * nq + myrow) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        u32x4 x = (myrow < nq) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, x);
+        for (int ks = 0; ks < KS; ks++) {
+            u32x4 x = (myrow < nq) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
     }
 
-    // ---- key/value sources
+    // ---- key/value rows of a tile (rows past the data are clamped to a real
+    // row: they are always masked, and their values stay finite)
     const size_t kvh = (size_t)b * a.Hkv + g;
     const __bf16 *klin = (const __bf16 *)a.k + kvh * (size_t)nq * D;
     const __bf16 *vlin = (const __bf16 *)a.v + kvh * (size_t)nq * D;
     const __bf16 *kring = (MODE == 1) ? (const __bf16 *)a.kc + kvh * (size_t)a.W * D : nullptr;
     const __bf16 *vring = (MODE == 1) ? (const __bf16 *)a.vc + kvh * (size_t)a.W * D : nullptr;
-    auto krow_ptr = [&](int kt, int j, const __bf16 *lin, const __bf16 *ring) -> const __bf16 * {
-        if (MODE == 1 && kt < kp.nrt) return ring + (size_t)(kt * BN + j) * D;
-        const int t = (kt - kp.nrt) * BN + j;
-        return (t < nq) ? lin + (size_t)t * D : nullptr;
+    auto row_off = [&](int kt, int j, bool &ring) -> size_t {
+        ring = (MODE == 1) && kt < kp.nrt;
+        if (ring) return (size_t)(kt * BN + j) * D;
+        int t = (kt - kp.nrt) * BN + j;
+        t = t < nq ? t : nq - 1;
+        return (size_t)t * D;
     };
+    // swizzles: logical 16-byte chunk c of row r sits at physical chunk c ^ swz(r)
+    auto kswz = [](int r) { return r & (CPR - 1); };
+    auto vswz = [](int r) { return ((r & 3) << 2) & (CPR - 1); };
 
-    u32x4 kreg[KLD];
-    u32x4 vreg[VLD][2];
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt, int stage) {
+        char *kdst = smem + stage * 2 * TILEB;
+        char *vdst = kdst + TILEB;
 #pragma unroll
-        for (int it = 0; it < KLD; it++) {
-            const int c = tid + NT * it;
-            const int j = c / DC, dc = c % DC;
-            const __bf16 *p = krow_ptr(kt, j, klin, kring);
-            kreg[it] = p ? ld16(p + dc * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int it = 0; it < VLD; it++) {
-            const int T = tid + NT * it;
-            const int kpi = (T & 15) + 16 * (T / (16 * DC));
-            const int dc = (T >> 4) % DC;
-            const __bf16 *p0 = krow_ptr(kt, 2 * kpi, vlin, vring);
-            const __bf16 *p1 = krow_ptr(kt, 2 * kpi + 1, vlin, vring);
-            vreg[it][0] = p0 ? ld16(p0 + dc * 8) : u32x4{0, 0, 0, 0};
-            vreg[it][1] = p1 ? ld16(p1 + dc * 8) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int it = 0; it < KLD; it++) {
-            const int c = tid + NT * it;
-            const int j = c / DC, dc = c % DC;
-            *(u32x4 *)(Ks + j * KROW + dc * 8) = kreg[it];
-        }
-#pragma unroll
-        for (int it = 0; it < VLD; it++) {
-            const int T = tid + NT * it;
-            const int kpi = (T & 15) + 16 * (T / (16 * DC));
-            const int dc = (T >> 4) % DC;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const uint32_t lo = (vreg[it][0][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                const uint32_t hi = (vreg[it][1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                *(uint32_t *)(Vt + (dc * 8 + e) * VROW + 2 * kpi) = lo | (hi << 16);
-            }
+        for (int i = 0; i < LPW; i++) {
+            const int ins = wave * LPW + i;
+            const int r = ins * RPL + lane / CPR;
+            const int pch = lane % CPR;
+            bool ring;
+            const size_t off = row_off(kt, r, ring);
+            const __bf16 *ks = (ring ? kring : klin) + off + (pch ^ kswz(r)) * 8;
+            const __bf16 *vs = (ring ? vring : vlin) + off + (pch ^ vswz(r)) * 8;
+            __builtin_amdgcn_global_load_lds((const void *)ks, (void *)(kdst + ins * 1024), 16, 0,
+                                             0);
+            __builtin_amdgcn_global_load_lds((const void *)vs, (void *)(vdst + ins * 1024), 16, 0,
+                                             0);
         }
     };
 
@@ -183,18 +177,24 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
     const int e0 = a.row_ptr[mrow], e1 = a.row_ptr[mrow + 1];
     const int qpos = qbase + myrow;
     const bool qvalid = myrow < qlen;
-    // ragged key tiles (beyond the array) always take the element mask
-    const int nlin_tiles_full = nq / BN;
+    const int nlin_full = nq / BN;  // linear tiles lying fully inside the data
 
-    if (e1 > e0) gload(a.col[e0]);
+    // per-lane constants of the two LDS read patterns
+    const int kr_row = lq;                       // + kb*32
+    const int tr_j = lane & 15;
+    const int tr_row = 4 * hh + (tr_j >> 2);     // + kk*16 + 8*r
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);  // + db*32
+
+    if (e1 > e0) issue(a.col[e0], 0);
     for (int e = e0; e < e1; e++) {
+        const int it = e - e0, stage = it & 1;
         const int kt = a.col[e];
-        const bool ragged = (kt - kp.nrt) >= nlin_tiles_full;
+        const bool ragged = (kt - kp.nrt) >= nlin_full;
         const bool partial = (a.col_cls[e] == 2) || ragged;
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (e + 1 < e1) gload(a.col[e + 1]);
+        __syncthreads();  // tile `it` is in LDS; every wave is done with tile it-1
+        if (e + 1 < e1) issue(a.col[e + 1], stage ^ 1);
+        const char *ksm = smem + stage * 2 * TILEB;
+        const char *vsm = ksm + TILEB;
 
         // element mask of this lane's 32 scores (bit kb*16 + i*4 + j)
         uint32_t vis = 0xffffffffu;
@@ -215,6 +215,7 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
                     }
             live[0] = __ballot((vis & 0xffffu) != 0) != 0;
             live[1] = __ballot((vis >> 16) != 0) != 0;
+            if (!live[0] && !live[1]) continue;
         }
 
         // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries
@@ -224,15 +225,17 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
 #pragma unroll
             for (int e2 = 0; e2 < 16; e2++) sacc[kb][e2] = 0.f;
             if (!live[kb]) continue;
-            const __bf16 *kr = Ks + (kb * 32 + lq) * KROW + hh * 8;
+            const int r = kb * 32 + kr_row;
+            const char *rowp = ksm + r * ROWB;
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kr + ks * 16));
+                const int c = (2 * ks + hh) ^ kswz(r);
+                bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rowp + c * 16));
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
             }
         }
 
-        // online softmax over this tile
+        // online softmax over this tile (exp2 domain)
         float mloc = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -241,10 +244,18 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
                 if (partial && !((vis >> (kb * 16 + e2)) & 1u)) sacc[kb][e2] = -INFINITY;
                 mloc = fmaxf(mloc, sacc[kb][e2]);
             }
-        mloc = wave_xor32_max(mloc);
-        const float m_new = fmaxf(m_run, mloc * c2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c2;
+        if (__ballot(mloc > m_run + RESCALE_SLACK) != 0) {
+            const float m_new = fmaxf(m_run, mloc);
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; db++)
+#pragma unroll
+                for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
@@ -254,37 +265,36 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
                 sacc[kb][e2] = pv;
                 psum += pv;
             }
-        psum = wave_xor32_sum(psum);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < DB; db++)
-#pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
+        l_run += psum + __shfl_xor(psum, 32);
 
-        // O^T += V^T P^T, 16 keys per step; the k index hh*8+t of both operands
-        // stands for key 16*s + 4*hh + t (t < 4) or 16*s + 8 + 4*hh + (t-4).
+        // O^T += V^T P^T in 16-key steps kk; the MFMA k index hh*8 + 4r + t of
+        // both operands stands for tile key 16kk + 8r + 4hh + t.
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
+        for (int kk = 0; kk < 4; kk++) {
+            const int kb = kk >> 1, s = kk & 1;
             if (!live[kb]) continue;
+            bf16x8 pf;
 #pragma unroll
-            for (int s = 0; s < 2; s++) {
-                bf16x8 pf;
+            for (int t = 0; t < 4; t++) {
+                pf[t] = (__bf16)sacc[kb][(2 * s) * 4 + t];
+                pf[4 + t] = (__bf16)sacc[kb][(2 * s + 1) * 4 + t];
+            }
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    pf[t] = (__bf16)sacc[kb][(2 * s) * 4 + t];
-                    pf[4 + t] = (__bf16)sacc[kb][(2 * s + 1) * 4 + t];
+            for (int db = 0; db < DB; db++) {
+                i16x4 v2[2];
+#pragma unroll
+                for (int r = 0; r < 2; r++) {
+                    const int row = kk * 16 + 8 * r + tr_row;
+                    const int col = db * 32 + tr_col;
+                    const int c = (col >> 3) ^ vswz(row);
+                    const char *p = vsm + row * ROWB + c * 16 + (col & 7) * 2;
+                    v2[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
                 }
-                const int kbase = kb * 32 + 16 * s + 4 * hh;
-#pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    const __bf16 *vr = Vt + (db * 32 + lq) * VROW + kbase;
-                    const u32x2 lo = *(const u32x2 *)(vr);
-                    const u32x2 hi = *(const u32x2 *)(vr + 8);
-                    const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, vv), pf, oacc[db], 0, 0, 0);
-                }
+                const u32x2 lo = __builtin_bit_cast(u32x2, v2[0]);
+                const u32x2 hi = __builtin_bit_cast(u32x2, v2[1]);
+                const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                                   pf, oacc[db], 0, 0, 0);
             }
         }
     }
@@ -307,9 +317,10 @@ __global__ __launch_bounds__(NW * 64) void tile_kernel(AttnArgs a) {
 
 template <int MODE, int D, int NW>
 hipError_t launch_one(const AttnArgs &a, hipStream_t s) {
-    const int nqt = (a.nq + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nqt, a.H, a.B);
-    hipLaunchKernelGGL((tile_kernel<MODE, D, NW>), grid, dim3(NW * 64), 0, s, a);
+    const long nqt = (a.nq + 32 * NW - 1) / (32 * NW);
+    const long total = nqt * a.H * a.B;
+    if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((tile_kernel<MODE, D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
