@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list: prefill,gqa,chunk,decode")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(scale for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -75,6 +78,15 @@ def main():
 
     only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode"}
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     K, WU = args.steps, args.warmup

@@ -50,26 +50,21 @@ constexpr float RESCALE_SLACK = 8.0f;  // exp2 arguments stay <= 8 between resca
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 
-// Logical position and validity of key `j` (0..BN-1) of key tile kt.
-template <int MODE>
+// Combine lane l with lane l^32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-request ring/metadata constants of a tile kernel.
 struct KeyPos {
     int nq, W, nrt, qlen, rs, cl, np;
-    __device__ __forceinline__ void at(int kt, int j, int &pos, bool &ok) const {
-        if (MODE == 0) {
-            pos = kt * BN + j;
-            ok = pos < qlen;
-        } else if (kt < nrt) {
-            const int s = kt * BN + j;
-            int r = s - rs;
-            r += (r < 0) ? W : 0;
-            ok = r < cl;
-            pos = np - cl + r;
-        } else {
-            const int t = (kt - nrt) * BN + j;
-            ok = t < nq;
-            pos = np + t;
-        }
-    }
 };
 
 // Workgroup p of T runs logical tile L: XCD x = p % 8 gets the contiguous
@@ -103,7 +98,7 @@ void tile_kernel(AttnArgs a) {
     const int G = a.H / a.Hkv;
     const int g = h / G;
 
-    KeyPos<MODE> kp;
+    KeyPos kp;
     kp.nq = nq;
     kp.W = a.W;
     kp.nrt = (MODE == 1) ? a.W / BN : 0;
@@ -196,43 +191,96 @@ void tile_kernel(AttnArgs a) {
         const char *ksm = smem + stage * 2 * TILEB;
         const char *vsm = ksm + TILEB;
 
-        // element mask of this lane's 32 scores (bit kb*16 + i*4 + j)
-        uint32_t vis = 0xffffffffu;
+        // Partial tiles: the tile keys this lane's query sees form one interval
+        // [a1, b1] of tile-local indices, plus a second one [a2, b2] only in a
+        // ring tile that holds the ring's wrap point (empty when b < a).
+        int a1 = 0, b1 = BN - 1, a2 = 0, b2 = -1;
         bool live[2] = {true, true};
+        bool two = false;
         if (partial) {
-            vis = 0;
+            const int lo_pos = qpos - a.W + 1;  // visible positions [lo_pos, qpos]
+            if (MODE == 0) {
+                const int base = kt * BN;       // position of tile key 0
+                a1 = lo_pos - base;
+                b1 = min(qpos, qlen - 1) - base;
+            } else if (kt < kp.nrt) {
+                const int off = kp.np - kp.cl;  // position of ring offset r = 0
+                const int rlo = max(0, lo_pos - off), rhi = min(kp.cl - 1, qpos - off);
+                const int base = kt * BN - kp.rs;  // r of tile key 0, before wrapping
+                if (base < 0 && base + BN > 0) {   // keys k < -base sit at r = base + k + W
+                    two = true;
+                    a1 = rlo - base - a.W;
+                    b1 = min(-base - 1, rhi - base - a.W);
+                    a2 = max(-base, rlo - base);
+                    b2 = rhi - base;
+                } else {
+                    const int rb = base < 0 ? base + a.W : base;
+                    a1 = rlo - rb;
+                    b1 = rhi - rb;
+                }
+            } else {
+                const int t0 = (kt - kp.nrt) * BN;  // new-row index of tile key 0
+                a1 = lo_pos - (kp.np + t0);
+                b1 = min(qpos - kp.np, nq - 1) - t0;
+            }
+            if (!qvalid) {
+                b1 = -1;
+                b2 = -1;
+            }
+            a1 = max(a1, 0);
+            b1 = min(b1, BN - 1);
+            a2 = max(a2, 0);
+            b2 = min(b2, BN - 1);
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        int pos;
-                        bool ok;
-                        kp.at(kt, kb * 32 + 8 * i + 4 * hh + j, pos, ok);
-                        ok = ok && qvalid && pos <= qpos && pos >= qpos - a.W + 1;
-                        vis |= (ok ? 1u : 0u) << (kb * 16 + i * 4 + j);
-                    }
-            live[0] = __ballot((vis & 0xffffu) != 0) != 0;
-            live[1] = __ballot((vis >> 16) != 0) != 0;
+            for (int kb = 0; kb < 2; kb++) {
+                const bool o1 = a1 <= b1 && a1 <= kb * 32 + 31 && b1 >= kb * 32;
+                const bool o2 = a2 <= b2 && a2 <= kb * 32 + 31 && b2 >= kb * 32;
+                live[kb] = __ballot(o1 || o2) != 0;
+            }
             if (!live[0] && !live[1]) continue;
         }
 
         // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries
         f32x16 sacc[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
+        for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int e2 = 0; e2 < 16; e2++) sacc[kb][e2] = 0.f;
-            if (!live[kb]) continue;
+        auto qk_step = [&](int kb, int ks) {
             const int r = kb * 32 + kr_row;
-            const char *rowp = ksm + r * ROWB;
+            const int c = (2 * ks + hh) ^ kswz(r);
+            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
+        };
+        if (live[0] && live[1]) {
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                const int c = (2 * ks + hh) ^ kswz(r);
-                bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4 *)(rowp + c * 16));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
+                qk_step(0, ks);
+                qk_step(1, ks);
             }
+        } else {
+            const int kb = live[0] ? 0 : 1;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) qk_step(kb, ks);
+        }
+        if (partial) {
+            // lane key of sacc[kb][4i+j] is kb*32 + 8i + 4hh + j
+            // key k is visible iff (unsigned)(k - a) <= b - a; an empty interval
+            // gets an offset that no tile key reaches
+            const bool e1 = b1 < a1, e2 = b2 < a2;
+            const int L1 = e1 ? -(1 << 20) : a1 - 4 * hh, L2 = e2 ? -(1 << 20) : a2 - 4 * hh;
+            const uint32_t n1 = e1 ? 0u : (uint32_t)(b1 - a1), n2 = e2 ? 0u : (uint32_t)(b2 - a2);
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int c = kb * 32 + 8 * i + j;
+                        bool vis = (uint32_t)(c - L1) <= n1;
+                        if (two) vis = vis || ((uint32_t)(c - L2) <= n2);
+                        if (!vis) sacc[kb][4 * i + j] = -INFINITY;
+                    }
         }
 
         // online softmax over this tile (exp2 domain)
@@ -240,11 +288,8 @@ void tile_kernel(AttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) {
-                if (partial && !((vis >> (kb * 16 + e2)) & 1u)) sacc[kb][e2] = -INFINITY;
-                mloc = fmaxf(mloc, sacc[kb][e2]);
-            }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c2;
+            for (int e2 = 0; e2 < 16; e2++) mloc = fmaxf(mloc, sacc[kb][e2]);
+        mloc = half_swap_max(mloc) * c2;
         if (__ballot(mloc > m_run + RESCALE_SLACK) != 0) {
             const float m_new = fmaxf(m_run, mloc);
             const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -265,7 +310,7 @@ void tile_kernel(AttnArgs a) {
                 sacc[kb][e2] = pv;
                 psum += pv;
             }
-        l_run += psum + __shfl_xor(psum, 32);
+        l_run += half_swap_sum(psum);
 
         // O^T += V^T P^T in 16-key steps kk; the MFMA k index hh*8 + 4r + t of
         // both operands stands for tile key 16kk + 8r + 4hh + t.
