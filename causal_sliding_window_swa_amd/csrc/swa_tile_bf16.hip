@@ -20,9 +20,13 @@
 //     B = the wave's 32 query rows kept in registers.  Each lane then holds
 //     one query column, so row max and sum need one swap across wave halves;
 //   * fp32 online softmax in the exp2 domain with the scale folded into one
-//     FMA; the running max is only raised (and O rescaled) when a row's tile
-//     max exceeds it by more than 8, which keeps every exp2 argument <= 8 and
-//     the result exact; rows whose max is still -inf use 0 (no -inf - -inf);
+//     FMA, against a reference max m_ref (0 to start) instead of the running
+//     max: p = exp2(s*c - m_ref) needs no max pass.  Only when a row's tile
+//     sum leaves [2^-32, 2^32] (overflow risk, or underflow before the row has
+//     seen a real max) does the wave recompute the tile's scores, take their
+//     max and rescale O and l (exact: O and l share the reference); p <= 2^32
+//     fits bf16 and fp32 with room to spare; the row sum is taken on the
+//     bf16-rounded P with v_dot2_f32_bf16, so it matches what PV uses;
 //   * O^T += V^T P^T: P comes straight from the S registers (rounded to bf16)
 //     and V^T from LDS with ds_read_b64_tr_b16, which transposes 4x4 blocks of
 //     16-bit values across lanes, so V stays row-major in LDS;
@@ -42,11 +46,13 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BN = 64;  // keys per tile
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float RESCALE_SLACK = 8.0f;  // exp2 arguments stay <= 8 between rescales
+constexpr float P_HI = 4294967296.0f;       // 2^32: tile sums above this rescale
+constexpr float P_LO = 2.3283064365386963e-10f;  // 2^-32: below this, before a real max
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 
@@ -129,39 +135,56 @@ void tile_kernel(AttnArgs a) {
     const __bf16 *vlin = (const __bf16 *)a.v + kvh * (size_t)nq * D;
     const __bf16 *kring = (MODE == 1) ? (const __bf16 *)a.kc + kvh * (size_t)a.W * D : nullptr;
     const __bf16 *vring = (MODE == 1) ? (const __bf16 *)a.vc + kvh * (size_t)a.W * D : nullptr;
-    auto row_off = [&](int kt, int j, bool &ring) -> size_t {
-        ring = (MODE == 1) && kt < kp.nrt;
-        if (ring) return (size_t)(kt * BN + j) * D;
-        int t = (kt - kp.nrt) * BN + j;
-        t = t < nq ? t : nq - 1;
-        return (size_t)t * D;
-    };
     // swizzles: logical 16-byte chunk c of row r sits at physical chunk c ^ swz(r)
     auto kswz = [](int r) { return r & (CPR - 1); };
     auto vswz = [](int r) { return ((r & 3) << 2) & (CPR - 1); };
 
+    // byte offsets of this lane's 16-byte pieces inside a tile (tile-invariant)
+    uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; i++) {
+        const int r = (wave * LPW + i) * RPL + lane / CPR;
+        const int pch = lane % CPR;
+        koff[i] = (uint32_t)(r * ROWB + (pch ^ kswz(r)) * 16);
+        voff[i] = (uint32_t)(r * ROWB + (pch ^ vswz(r)) * 16);
+    }
     auto issue = [&](int kt, int stage) {
         char *kdst = smem + stage * 2 * TILEB;
         char *vdst = kdst + TILEB;
+        const bool ring = (MODE == 1) && kt < kp.nrt;
+        const int t0 = ring ? kt * BN : (kt - kp.nrt) * BN;  // first row of the tile
+        const char *kb = (const char *)((ring ? kring : klin) + (size_t)t0 * D);
+        const char *vb = (const char *)((ring ? vring : vlin) + (size_t)t0 * D);
+        if (ring || t0 + BN <= nq) {
 #pragma unroll
-        for (int i = 0; i < LPW; i++) {
-            const int ins = wave * LPW + i;
-            const int r = ins * RPL + lane / CPR;
-            const int pch = lane % CPR;
-            bool ring;
-            const size_t off = row_off(kt, r, ring);
-            const __bf16 *ks = (ring ? kring : klin) + off + (pch ^ kswz(r)) * 8;
-            const __bf16 *vs = (ring ? vring : vlin) + off + (pch ^ vswz(r)) * 8;
-            __builtin_amdgcn_global_load_lds((const void *)ks, (void *)(kdst + ins * 1024), 16, 0,
-                                             0);
-            __builtin_amdgcn_global_load_lds((const void *)vs, (void *)(vdst + ins * 1024), 16, 0,
-                                             0);
+            for (int i = 0; i < LPW; i++) {
+                const int ins = wave * LPW + i;
+                __builtin_amdgcn_global_load_lds((const void *)(kb + koff[i]),
+                                                 (void *)(kdst + ins * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vb + voff[i]),
+                                                 (void *)(vdst + ins * 1024), 16, 0, 0);
+            }
+        } else {  // ragged last tile: rows past the data are clamped to the last row
+#pragma unroll
+            for (int i = 0; i < LPW; i++) {
+                const int ins = wave * LPW + i;
+                const int r = ins * RPL + lane / CPR;
+                const int rc = (t0 + r < nq) ? r : nq - 1 - t0;  // 0 <= rc < nq - t0
+                // same chunk, row rc: a non-negative offset inside the data
+                const int ko = (int)koff[i] + (rc - r) * ROWB;
+                const int vo = (int)voff[i] + (rc - r) * ROWB;
+                __builtin_amdgcn_global_load_lds((const void *)(kb + ko),
+                                                 (void *)(kdst + ins * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vb + vo),
+                                                 (void *)(vdst + ins * 1024), 16, 0, 0);
+            }
         }
     };
 
     // ---- running softmax state: lanes l and l^32 share query column lq
     const float c2 = a.scale * LOG2E;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = 0.f, l_run = 0.f;  // p = exp2(s*c2 - m_ref); O, l share m_ref
+    bool guess = true;               // m_ref not yet taken from a real max
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; db++)
@@ -240,90 +263,111 @@ void tile_kernel(AttnArgs a) {
             if (!live[0] && !live[1]) continue;
         }
 
-        // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries
+        // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries;
+        // masked scores become -inf
         f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) sacc[kb][e2] = 0.f;
-        auto qk_step = [&](int kb, int ks) {
-            const int r = kb * 32 + kr_row;
-            const int c = (2 * ks + hh) ^ kswz(r);
-            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
-        };
-        if (live[0] && live[1]) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                qk_step(0, ks);
-                qk_step(1, ks);
-            }
-        } else {
-            const int kb = live[0] ? 0 : 1;
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) qk_step(kb, ks);
-        }
-        if (partial) {
-            // lane key of sacc[kb][4i+j] is kb*32 + 8i + 4hh + j
-            // key k is visible iff (unsigned)(k - a) <= b - a; an empty interval
-            // gets an offset that no tile key reaches
-            const bool e1 = b1 < a1, e2 = b2 < a2;
-            const int L1 = e1 ? -(1 << 20) : a1 - 4 * hh, L2 = e2 ? -(1 << 20) : a2 - 4 * hh;
-            const uint32_t n1 = e1 ? 0u : (uint32_t)(b1 - a1), n2 = e2 ? 0u : (uint32_t)(b2 - a2);
+        auto scores = [&]() {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int e2 = 0; e2 < 16; e2++) sacc[kb][e2] = 0.f;
+            auto qk_step = [&](int kb, int ks) {
+                const int r = kb * 32 + kr_row;
+                const int c = (2 * ks + hh) ^ kswz(r);
+                const bf16x8 af =
+                    __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
+            };
+            if (live[0] && live[1]) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int c = kb * 32 + 8 * i + j;
-                        bool vis = (uint32_t)(c - L1) <= n1;
-                        if (two) vis = vis || ((uint32_t)(c - L2) <= n2);
-                        if (!vis) sacc[kb][4 * i + j] = -INFINITY;
-                    }
-        }
-
-        // online softmax over this tile (exp2 domain)
-        float mloc = -INFINITY;
+                for (int ks = 0; ks < KS; ks++) {
+                    qk_step(0, ks);
+                    qk_step(1, ks);
+                }
+            } else if (live[0]) {
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+                for (int ks = 0; ks < KS; ks++) qk_step(0, ks);
+            } else {
 #pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) mloc = fmaxf(mloc, sacc[kb][e2]);
-        mloc = half_swap_max(mloc) * c2;
-        if (__ballot(mloc > m_run + RESCALE_SLACK) != 0) {
-            const float m_new = fmaxf(m_run, mloc);
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; db++)
-#pragma unroll
-                for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e2], c2, -m_use));
-                sacc[kb][e2] = pv;
-                psum += pv;
+                for (int ks = 0; ks < KS; ks++) qk_step(1, ks);
             }
-        l_run += half_swap_sum(psum);
+            if (partial) {
+                // key k is visible iff (unsigned)(k - a) <= b - a; an empty interval
+                // gets an offset that no tile key reaches.  Lane key of
+                // sacc[kb][4i+j] is kb*32 + 8i + 4hh + j.
+                const bool x1 = b1 < a1, x2 = !two || b2 < a2;
+                const int L1 = x1 ? -(1 << 20) : a1 - 4 * hh, L2 = x2 ? -(1 << 20) : a2 - 4 * hh;
+                const uint32_t n1 = x1 ? 0u : (uint32_t)(b1 - a1);
+                const uint32_t n2 = x2 ? 0u : (uint32_t)(b2 - a2);
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            const int c = kb * 32 + 8 * i + j;
+                            const bool vis =
+                                ((uint32_t)(c - L1) <= n1) | ((uint32_t)(c - L2) <= n2);
+                            sacc[kb][4 * i + j] = vis ? sacc[kb][4 * i + j] : -INFINITY;
+                        }
+            }
+        };
+        // P = exp2(S*c2 - m_ref) rounded to bf16, packed as the PV B operands
+        // (pk[kk] for 16-key step kk), and this tile's row sum of P
+        bf16x8 pk[4];
+        auto probs = [&]() -> float {
+            float acc = 0.f;
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                const int kb = kk >> 1, s2 = kk & 1;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    pk[kk][t] = (__bf16)__builtin_amdgcn_exp2f(
+                        fmaf(sacc[kb][(2 * s2) * 4 + t], c2, -m_ref));
+                    pk[kk][4 + t] = (__bf16)__builtin_amdgcn_exp2f(
+                        fmaf(sacc[kb][(2 * s2 + 1) * 4 + t], c2, -m_ref));
+                }
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const bf16x2 pr = {pk[kk][2 * t], pk[kk][2 * t + 1]};
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+                }
+            }
+            return half_swap_sum(acc);
+        };
+        scores();
+        float psum = probs();
+        const bool lane_vis = !partial || (b1 >= a1) || (two && b2 >= a2);
+        const bool rare = psum > P_HI || (guess && lane_vis && psum < P_LO);
+        if (__ballot(rare) != 0) {
+            // take the real max of this tile's scores and move the reference
+            scores();
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e2 = 0; e2 < 16; e2++) mloc = fmaxf(mloc, sacc[kb][e2]);
+            mloc = half_swap_max(mloc) * c2;
+            if (mloc != -INFINITY && (guess || mloc > m_ref)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - mloc);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; db++)
+#pragma unroll
+                    for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
+                m_ref = mloc;
+                guess = false;
+            }
+            psum = probs();
+        }
+        l_run += psum;
 
         // O^T += V^T P^T in 16-key steps kk; the MFMA k index hh*8 + 4r + t of
         // both operands stands for tile key 16kk + 8r + 4hh + t.
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
-            const int kb = kk >> 1, s = kk & 1;
-            if (!live[kb]) continue;
-            bf16x8 pf;
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                pf[t] = (__bf16)sacc[kb][(2 * s) * 4 + t];
-                pf[4 + t] = (__bf16)sacc[kb][(2 * s + 1) * 4 + t];
-            }
+            if (!live[kk >> 1]) continue;
 #pragma unroll
             for (int db = 0; db < DB; db++) {
                 i16x4 v2[2];
@@ -339,7 +383,7 @@ void tile_kernel(AttnArgs a) {
                 const u32x2 hi = __builtin_bit_cast(u32x2, v2[1]);
                 const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                                   pf, oacc[db], 0, 0, 0);
+                                                                   pk[kk], oacc[db], 0, 0, 0);
             }
         }
     }
