@@ -11,6 +11,8 @@
 //   * fp32 online softmax per head (exp2, scale folded into one FMA);
 //   * probabilities go through a small per-wave LDS table to the lanes that
 //     hold V rows (16 lanes x 16 bytes per row), which accumulate P V in fp32;
+//   * each wave walks its quarter in 32-key steps with two register buffers,
+//     so the next step's K/V loads are in flight while one step computes;
 //   * the 4 waves merge in LDS; each range writes (max, sum, unnormalised O)
 //     to the workspace, and a second kernel merges the ranges by log-sum-exp.
 //
@@ -33,10 +35,38 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int CH = 64;    // keys per wave iteration
+constexpr int CH = 32;    // keys per wave iteration (two register buffers in flight)
 constexpr int PST = 20;   // LDS probability row stride (floats): conflict-free writes
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+
+// Combine lane l with lane l^16 / l^32 without an LDS round trip.
+__device__ __forceinline__ float swap16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// lane-xor sum for the end-of-range merge (offsets 8, 16 or 32)
+__device__ __forceinline__ float xor_sum(float x, int off) {
+    if (off == 16) return swap16_sum(x);
+    if (off == 32) return swap32_sum(x);
+    return x + __shfl_xor(x, off);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -62,7 +92,6 @@ struct RingView {
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     constexpr int KSTEP = D / 32;  // 32-wide k-steps of the QK product
-    constexpr int DQ = D / 4;      // d values per lane group in the QK operands
     constexpr int LPR = D / 8;     // lanes per V row (16 bytes each)
     constexpr int RPI = 64 / LPR;  // V rows per wave instruction
     constexpr int NRR = CH / RPI;  // V row rounds per iteration
@@ -106,13 +135,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         *(u32x4 *)((__bf16 *)a.vc + (kvh * W + rv.s_new) * D + tid * 8) = ld16(vnew + tid * 8);
     }
 
-    // Q of the group as the B operand: column lh = head (zero past G)
+    // Q of the group as the B operand: column lh = head (zero past G).  The MFMA
+    // k index lg*8 + t of k-step ks stands for d = ks*32 + lg*8 + t in both
+    // operands, so the 4 lanes of one K row read 64 contiguous bytes per load.
     bf16x8 qf[KSTEP];
     {
-        const __bf16 *qp = (const __bf16 *)a.q + ((size_t)b * a.H + g * G + lh) * D + lg * DQ;
+        const __bf16 *qp = (const __bf16 *)a.q + ((size_t)b * a.H + g * G + lh) * D + lg * 8;
 #pragma unroll
         for (int ks = 0; ks < KSTEP; ks++) {
-            u32x4 x = (lh < G) ? ld16(qp + ks * 8) : u32x4{0, 0, 0, 0};
+            u32x4 x = (lh < G) ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -126,39 +157,41 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; e++) o[hq][e] = 0.f;
     float *P = Pl[wave];
 
-    for (int it = 0; it < niter; it++) {
-        const int c0 = w0 + it * CH;
-        // issue every load of this iteration: K (MFMA layout), then V rows
-        u32x4 kr[4][KSTEP];
+    // one iteration's loads: K in the MFMA A layout, V as 16-byte row pieces
+    struct Buf {
+        u32x4 k[2][KSTEP];
+        u32x4 v[NRR];
+    };
+    auto load = [&](Buf &bf, int c0) {
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
+        for (int kb = 0; kb < 2; kb++) {
             const int s = c0 + kb * 16 + lh;
             const __bf16 *src = (s == rv.s_new) ? knew : kring + (size_t)s * D;
 #pragma unroll
             for (int ks = 0; ks < KSTEP; ks++)
-                kr[kb][ks] = (s < w1) ? ld16(src + lg * DQ + ks * 8) : u32x4{0, 0, 0, 0};
+                bf.k[kb][ks] = (s < w1) ? ld16(src + ks * 32 + lg * 8) : u32x4{0, 0, 0, 0};
         }
-        u32x4 vr[NRR];
 #pragma unroll
         for (int rr = 0; rr < NRR; rr++) {
             const int s = c0 + rr * RPI + lane / LPR;
             const __bf16 *src = (s == rv.s_new) ? vnew : vring + (size_t)s * D;
-            vr[rr] = (s < w1) ? ld16(src + (lane % LPR) * 8) : u32x4{0, 0, 0, 0};
+            bf.v[rr] = (s < w1) ? ld16(src + (lane % LPR) * 8) : u32x4{0, 0, 0, 0};
         }
-
+    };
+    auto compute = [&](const Buf &bf, int c0) {
         // scores: sacc[kb][j] = S[key c0 + kb*16 + lg*4 + j][head lh]
-        f32x4 sacc[4];
+        f32x4 sacc[2];
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
+        for (int kb = 0; kb < 2; kb++) {
             sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSTEP; ks++)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, kr[kb][ks]), qf[ks], sacc[kb], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, bf.k[kb][ks]), qf[ks], sacc[kb], 0, 0, 0);
         }
         float mloc = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++)
+        for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int s = c0 + kb * 16 + lg * 4 + j;
@@ -167,28 +200,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 if (!ok) sacc[kb][j] = -INFINITY;
                 mloc = fmaxf(mloc, sacc[kb][j]);
             }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = swap32_max(swap16_max(mloc));
         const float m_new = fmaxf(m_run, mloc * c2);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++)
+        for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], c2, -m_use));
                 psum += p;
                 P[(kb * 16 + lg * 4 + j) * PST + lh] = p;
             }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
+        psum = swap32_sum(swap16_sum(psum));
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // rescale O by each head's alpha (held by lane hq)
 #pragma unroll
         for (int hq = 0; hq < G; hq++) {
-            const float ah = __shfl(alpha, hq);
+            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hq));
 #pragma unroll
             for (int e = 0; e < 8; e++) o[hq][e] *= ah;
         }
@@ -212,8 +243,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                v[2 * e] = bf_lo(vr[rr][e]);
-                v[2 * e + 1] = bf_hi(vr[rr][e]);
+                v[2 * e] = bf_lo(bf.v[rr][e]);
+                v[2 * e + 1] = bf_hi(bf.v[rr][e]);
             }
 #pragma unroll
             for (int hq = 0; hq < G; hq++)
@@ -221,6 +252,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                 for (int e = 0; e < 8; e++) o[hq][e] = fmaf(pr[hq], v[e], o[hq][e]);
         }
         wave_lds_order();
+    };
+    // two buffers: the next iteration's loads are in flight while one computes
+    Buf b0, b1;
+    if (niter > 0) load(b0, w0);
+    for (int it = 0; it < niter; it += 2) {
+        if (it + 1 < niter) load(b1, w0 + (it + 1) * CH);
+        compute(b0, w0 + it * CH);
+        if (it + 1 < niter) {
+            if (it + 2 < niter) load(b0, w0 + (it + 2) * CH);
+            compute(b1, w0 + (it + 1) * CH);
+        }
     }
 
     // sum the row groups of the wave (lanes with equal lane % LPR)
@@ -229,7 +271,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int hq = 0; hq < G; hq++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) o[hq][e] += __shfl_xor(o[hq][e], off);
+            for (int e = 0; e < 8; e++) o[hq][e] = xor_sum(o[hq][e], off);
     if (lane < 16) {
         wm[wave][lane] = m_run;
         wl[wave][lane] = l_run;
@@ -315,8 +357,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Ranges per (request, KV head): enough workgroups to fill the chip, each
-// range at least 256 slots (64 per wave).
+// Ranges per (request, KV head): each range is at least 256 slots (64 per
+// wave); the workspace is sized for this maximum.
 int decode_max_splits(int W) {
     int m = W / 256;
     if (m < 1) m = 1;
@@ -324,12 +366,14 @@ int decode_max_splits(int W) {
     return m;
 }
 
+// Enough workgroups (about 8192) to keep many loads in flight on every CU;
+// never more ranges than the workspace holds.
 int decode_bf16_splits(int B, int Hkv, int W) {
     const long pairs = (long)B * Hkv;
+    const int cap = decode_max_splits(W);
     int n = 1;
-    while (pairs * n < 2048 && n < decode_max_splits(W)) n <<= 1;
-    if (n > decode_max_splits(W)) n = decode_max_splits(W);
-    return n;
+    while (pairs * n < 8192 && n < cap) n <<= 1;
+    return n < cap ? n : cap;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {

@@ -92,7 +92,11 @@ void tile_kernel(AttnArgs a) {
     constexpr int TILEB = BN * ROWB;    // bytes per K (or V) tile
     static_assert(LPW >= 1, "tile too small for the block");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];  // [stage][K, V]
+    // two stages [K tile | V tile]; separate arrays so that the compiler can
+    // tell the reads of one stage from the LDS-DMA writes into the other (else
+    // it waits for the next tile's loads before every LDS read)
+    __shared__ __attribute__((aligned(1024))) char stage0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char stage1[2 * TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,8 +152,7 @@ void tile_kernel(AttnArgs a) {
         koff[i] = (uint32_t)(r * ROWB + (pch ^ kswz(r)) * 16);
         voff[i] = (uint32_t)(r * ROWB + (pch ^ vswz(r)) * 16);
     }
-    auto issue = [&](int kt, int stage) {
-        char *kdst = smem + stage * 2 * TILEB;
+    auto issue = [&](int kt, char *kdst) {
         char *vdst = kdst + TILEB;
         const bool ring = (MODE == 1) && kt < kp.nrt;
         const int t0 = ring ? kt * BN : (kt - kp.nrt) * BN;  // first row of the tile
@@ -203,16 +206,15 @@ void tile_kernel(AttnArgs a) {
     const int tr_row = 4 * hh + (tr_j >> 2);     // + kk*16 + 8*r
     const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);  // + db*32
 
-    if (e1 > e0) issue(a.col[e0], 0);
-    for (int e = e0; e < e1; e++) {
-        const int it = e - e0, stage = it & 1;
+    // one tile: compute on `cur` while the next tile streams into `nxt`
+    auto tile = [&](int e, const char *cur, char *nxt) {
         const int kt = a.col[e];
         const bool ragged = (kt - kp.nrt) >= nlin_full;
         const bool partial = (a.col_cls[e] == 2) || ragged;
-        __syncthreads();  // tile `it` is in LDS; every wave is done with tile it-1
-        if (e + 1 < e1) issue(a.col[e + 1], stage ^ 1);
-        const char *ksm = smem + stage * 2 * TILEB;
-        const char *vsm = ksm + TILEB;
+        __syncthreads();  // this tile is in LDS; every wave is done with the previous one
+        if (e + 1 < e1) issue(a.col[e + 1], nxt);
+        const char *ksm = cur;
+        const char *vsm = cur + TILEB;
 
         // Partial tiles: the tile keys this lane's query sees form one interval
         // [a1, b1] of tile-local indices, plus a second one [a2, b2] only in a
@@ -260,7 +262,7 @@ void tile_kernel(AttnArgs a) {
                 const bool o2 = a2 <= b2 && a2 <= kb * 32 + 31 && b2 >= kb * 32;
                 live[kb] = __ballot(o1 || o2) != 0;
             }
-            if (!live[0] && !live[1]) continue;
+            if (!live[0] && !live[1]) return;
         }
 
         // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries;
@@ -386,6 +388,11 @@ void tile_kernel(AttnArgs a) {
                                                                    pk[kk], oacc[db], 0, 0, 0);
             }
         }
+    };
+    if (e1 > e0) issue(a.col[e0], stage0);
+    for (int e = e0; e < e1; e += 2) {
+        tile(e, stage0, stage1);
+        if (e + 1 < e1) tile(e + 1, stage1, stage0);
     }
 
     // ---- epilogue: O = O / l; rows without any visible key (padding) get 0
