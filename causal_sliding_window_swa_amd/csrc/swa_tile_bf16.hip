@@ -10,8 +10,12 @@
 //
 // Work split (tile_q = 32 * NW query rows, tile_k = 64 keys, head dim D):
 //   * one workgroup per (query tile, head, batch), ordered so that each XCD
-//     walks a contiguous range of query tiles (neighbouring tiles share most
-//     of their K/V rows, which then hit in that XCD's L2);
+//     walks a contiguous range of (query tile, head) pairs with the query
+//     heads of one KV group next to each other: they read identical K/V tiles,
+//     and neighbouring query tiles share most of theirs, so both hit in that
+//     XCD's L2;
+//   * wave priority is raised over the MFMA sections, so that while one wave
+//     issues its matrix work the co-resident wave fills the VALU slots;
 //   * K and V tiles go straight from HBM to LDS (global_load_lds_dwordx4, no
 //     register staging), double-buffered: the next tile streams in while this
 //     one is computed; rows are XOR-swizzled in 16-byte chunks so that both
@@ -103,10 +107,13 @@ void tile_kernel(AttnArgs a) {
     const int lq = lane & 31, hh = lane >> 5;
     const int nq = a.nq;
     const int nqt = (nq + 32 * NW - 1) / (32 * NW);
+    // logical order: query heads of one KV group adjacent (they read the same
+    // K/V tiles), then query tiles, then KV heads, then requests
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = L % nqt, h = (L / nqt) % a.H, b = L / (nqt * a.H);
     const int G = a.H / a.Hkv;
-    const int g = h / G;
+    const int h_in = L % G, qt = (L / G) % nqt, g = (L / (G * nqt)) % a.Hkv;
+    const int b = L / (G * nqt * a.Hkv);
+    const int h = g * G + h_in;
 
     KeyPos kp;
     kp.nq = nq;
@@ -338,7 +345,9 @@ void tile_kernel(AttnArgs a) {
             }
             return half_swap_sum(acc);
         };
+        __builtin_amdgcn_s_setprio(2);
         scores();
+        __builtin_amdgcn_s_setprio(0);
         float psum = probs();
         const bool lane_vis = !partial || (b1 >= a1) || (two && b2 >= a2);
         const bool rare = psum > P_HI || (guess && lane_vis && psum < P_LO);
@@ -365,6 +374,7 @@ void tile_kernel(AttnArgs a) {
         }
         l_run += psum;
 
+        __builtin_amdgcn_s_setprio(2);
         // O^T += V^T P^T in 16-key steps kk; the MFMA k index hh*8 + 4r + t of
         // both operands stands for tile key 16kk + 8r + 4hh + t.
 #pragma unroll
@@ -388,6 +398,7 @@ void tile_kernel(AttnArgs a) {
                                                                    pk[kk], oacc[db], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     if (e1 > e0) issue(a.col[e0], stage0);
     for (int e = e0; e < e1; e += 2) {
