@@ -13,14 +13,16 @@
 //     hold V rows (16 lanes x 16 bytes per row), which accumulate P V in fp32;
 //   * each wave walks its quarter in 32-key steps with two register buffers,
 //     so the next step's K/V loads are in flight while one step computes;
-//   * the 4 waves merge in LDS; each range writes (max, sum, unnormalised O)
-//     to the workspace, and a second kernel merges the ranges by log-sum-exp.
+//   * the waves merge in LDS; a single range writes O directly (a tiny kernel
+//     then advances the ring state), otherwise each range writes (max, sum,
+//     unnormalised O) to the workspace and a second kernel merges the ranges
+//     by log-sum-exp and advances the state.
 //
 // Append first ("Dense vs sliding-window sparse attention" blog §3.2 rule):
 // the new row goes to slot (ring_start + cache_len) mod W while the ring is
 // filling, else over the oldest slot ring_start.  The range owning that slot
 // reads the new row from k_new/v_new and writes it into the ring; no other
-// block reads that slot.  The ring state itself is advanced by the combine
+// block reads that slot.  The ring state itself is advanced by a second
 // kernel, after every range has read it.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -89,16 +91,16 @@ struct RingView {
     }
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+template <int D, int G, int NWV>
+__global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
     constexpr int KSTEP = D / 32;  // 32-wide k-steps of the QK product
     constexpr int LPR = D / 8;     // lanes per V row (16 bytes each)
     constexpr int RPI = 64 / LPR;  // V rows per wave instruction
     constexpr int NRR = CH / RPI;  // V row rounds per iteration
 
-    __shared__ __attribute__((aligned(16))) float Pl[4][CH * PST];
-    __shared__ float wm[4][16], wl[4][16];
-    __shared__ float wo[4][G][D];
+    __shared__ __attribute__((aligned(16))) float Pl[NWV][CH * PST];
+    __shared__ float wm[NWV][16], wl[NWV][16];
+    __shared__ float wo[NWV][G][D];
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     // slot ranges: split -> [s0, s1), wave -> [w0, w1)
     const int S = (W + a.n_split - 1) / a.n_split;
     const int s0 = split * S, s1 = min(W, s0 + S);
-    const int SW = (S + 3) / 4;
+    const int SW = (S + NWV - 1) / NWV;
     const int w0 = s0 + wave * SW, w1 = min(s1, w0 + SW);
     const int niter = (SW + CH - 1) / CH;  // same for every wave of the block
 
@@ -283,20 +285,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             for (int e = 0; e < 8; e++) wo[wave][hq][lane * 8 + e] = o[hq][e];
     }
     __syncthreads();
-    // merge the 4 waves; write this range's (max, sum, unnormalised O)
+    // merge the waves; with one range per (request, KV head) write O itself,
+    // else this range's (max, sum, unnormalised O)
     const int nsp = a.n_split;
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < G * D; idx += NWV * 64) {
         const int hq = idx / D, dd = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; w++) M = fmaxf(M, wm[w][hq]);
+        for (int w = 0; w < NWV; w++) M = fmaxf(M, wm[w][hq]);
         const float Mu = (M == -INFINITY) ? 0.f : M;
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
+        for (int w = 0; w < NWV; w++) {
             const float f = __builtin_amdgcn_exp2f(wm[w][hq] - Mu);
             L += f * wl[w][hq];
             O += f * wo[w][hq][dd];
+        }
+        if (nsp == 1) {
+            ((__bf16 *)a.o)[((size_t)b * a.H + g * G + hq) * D + dd] =
+                (__bf16)((L > 0.f) ? O / L : 0.f);
+            continue;
         }
         const size_t hidx = ((size_t)b * a.H + g * G + hq) * nsp + split;
         a.ws[hidx * D + dd] = O;
@@ -308,22 +316,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// grid (B*H), D threads: log-sum-exp merge of the ranges, O = sum / l as bf16;
-// block (b, head 0) then advances the ring state of request b by one token.
-template <int D>
+// grid (B*H), D threads: log-sum-exp merge of the NSP ranges, O = sum / l as
+// bf16; block (b, head 0) then advances the ring state of request b by one
+// token.  NSP is a compile-time constant so every (max, sum) pair (uniform
+// across the block, hence scalar loads) and partial row is loaded before any
+// is used.
+template <int D, int NSP>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-    const int nsp = a.n_split;
-    const float *ml = a.ws + (size_t)a.B * a.H * nsp * D;
+    const float *ml = a.ws + (size_t)a.B * a.H * NSP * D + (size_t)bh * NSP * 2;
+    const float *op = a.ws + (size_t)bh * NSP * D + threadIdx.x;
+    float m[NSP], l[NSP], o[NSP];
+#pragma unroll
+    for (int s = 0; s < NSP; s++) {
+        m[s] = ml[2 * s];
+        l[s] = ml[2 * s + 1];
+        o[s] = op[(size_t)s * D];
+    }
     float M = -INFINITY;
-    for (int s = 0; s < nsp; s++) M = fmaxf(M, ml[2 * ((size_t)bh * nsp + s)]);
+#pragma unroll
+    for (int s = 0; s < NSP; s++) M = fmaxf(M, m[s]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, O = 0.f;
-    for (int s = 0; s < nsp; s++) {
-        const size_t hidx = (size_t)bh * nsp + s;
-        const float f = __builtin_amdgcn_exp2f(ml[2 * hidx] - Mu);
-        L += f * ml[2 * hidx + 1];
-        O += f * a.ws[hidx * D + threadIdx.x];
+#pragma unroll
+    for (int s = 0; s < NSP; s++) {
+        const float f = __builtin_amdgcn_exp2f(m[s] - Mu);
+        L += f * l[s];
+        O += f * o[s];
     }
     ((__bf16 *)a.o)[(size_t)bh * D + threadIdx.x] = (__bf16)((L > 0.f) ? O / L : 0.f);
     if (h == 0 && threadIdx.x == 0) {
@@ -335,13 +354,44 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     }
 }
 
+// Advances the ring state of every request by one token (after the single-
+// range kernel, which writes O itself).
+__global__ void decode_state_kernel(int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                                    int B, int W) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int rs = ring_start[b], cl = cache_len[b];
+    const bool full = cl == W;
+    ring_start[b] = full ? (rs + 1) % W : rs;
+    cache_len[b] = full ? W : cl + 1;
+    next_pos[b] = next_pos[b] + 1;
+}
+
+// One range per (request, KV head): the waves merge in LDS and write O, then
+// the ring state advances.  Several ranges: the log-sum-exp combine follows.
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(a.n_split, a.Hkv, a.B), dim3(256), 0, s,
-                       a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D), 0, s, a);
+    hipError_t e;
+    if (a.n_split == 1) {
+        hipLaunchKernelGGL((decode_split_kernel<D, G, 4>), dim3(1, a.Hkv, a.B), dim3(256), 0, s,
+                           a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_state_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s,
+                           a.ring_start, a.cache_len, a.next_pos, a.B, a.W);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_split_kernel<D, G, 4>), dim3(a.n_split, a.Hkv, a.B), dim3(256), 0,
+                       s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 grid(a.B * a.H), blk(D);
+    switch (a.n_split) {
+        case 2: hipLaunchKernelGGL((decode_combine_kernel<D, 2>), grid, blk, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_combine_kernel<D, 4>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_combine_kernel<D, 8>), grid, blk, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_combine_kernel<D, 16>), grid, blk, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_combine_kernel<D, 32>), grid, blk, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -357,23 +407,23 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Ranges per (request, KV head): each range is at least 256 slots (64 per
-// wave); the workspace is sized for this maximum.
+// Ranges per (request, KV head): a power of two, each range at least 256
+// slots (64 per wave), at most 32 (the combine kernel's instantiations); the
+// workspace is sized for this maximum.
 int decode_max_splits(int W) {
-    int m = W / 256;
-    if (m < 1) m = 1;
-    if (m > 32) m = 32;
+    int m = 1;
+    while (m < 32 && 2 * m * 256 <= W) m <<= 1;
     return m;
 }
 
-// Enough workgroups (about 8192) to keep many loads in flight on every CU;
-// never more ranges than the workspace holds.
+// Enough ranges for about 8192 workgroups (many short workgroups keep the
+// CUs fuller than a few long ones), never more than the workspace holds.
 int decode_bf16_splits(int B, int Hkv, int W) {
     const long pairs = (long)B * Hkv;
     const int cap = decode_max_splits(W);
     int n = 1;
     while (pairs * n < 8192 && n < cap) n <<= 1;
-    return n < cap ? n : cap;
+    return n;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {

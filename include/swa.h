@@ -161,7 +161,7 @@ size_t swa_decode_workspace_size(int B, int H, int d, int W);
  * next_pos (the old value) attends over the ring's valid slots; next_pos
  * grows by one.  workspace: device memory of swa_decode_workspace_size bytes
  * (ws_bytes), no initialisation needed.
- * Supported: SWA_BF16 with d in {64, 128}, H / Hkv <= 16; SWA_F32 with d a
+ * Supported: SWA_BF16 with d in {64, 128}, H / Hkv in {1, 2, 4, 8}; SWA_F32 with d a
  * multiple of 4 in [4, 128].
  * Errors: as swa_fwd, plus SWA_EINVAL when ws_bytes is too small. */
 int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W,
