@@ -73,6 +73,11 @@ class Oracle:
         lib.orc_blockmask.argtypes = [i, i, i, i, i, i, P, P, P, P, i, P, P, P,
                                       P, P, P, P, P]
         lib.orc_blockmask.restype = ctypes.c_int64
+        lib.orc_bwd.argtypes = [i, i, i, i, i, i, P, P, P, P, P, d, P, P, P, P]
+        lib.orc_bwd.restype = None
+        lib.orc_bwd_sel.argtypes = [i, i, i, i, i, i, P, P, P, P, P, d, i, P, P, P, P, i, P,
+                                    P, P, P, P]
+        lib.orc_bwd_sel.restype = None
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -105,6 +110,40 @@ class Oracle:
                               float(scale), rows.shape[0], _ptr(rb), _ptr(rh), _ptr(ri),
                               _ptr(out))
         return out
+
+    def bwd(self, q, k, v, dout, W: int, scale: float, q_len=None):
+        """Gradients of the full-sequence forward for output gradient dout.
+        Returns (dq [B,H,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d], lse [B,H,N]); lse is
+        the natural-log log-sum-exp of each row's allowed scores (-inf if none)."""
+        q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+        B, H, N, dd = q.shape
+        Hkv = k.shape[1]
+        ql = _i32(q_len)
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        lse = np.empty((B, H, N), dtype=np.float64)
+        self.lib.orc_bwd(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ql),
+                         float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(lse))
+        return dq, dk, dv, lse
+
+    def bwd_sel(self, q, k, v, dout, W: int, scale: float, qrows, keys, q_len=None):
+        """Gradients for selected entries: dq of rows qrows [n,3] (b, h, i) and
+        dk, dv of keys keys [m,3] (b, g, j).  Returns (dq [n,d], dk [m,d], dv [m,d])."""
+        q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+        B, H, N, dd = q.shape
+        Hkv = k.shape[1]
+        ql = _i32(q_len)
+        qrows = np.asarray(qrows, dtype=np.int32).reshape(-1, 3)
+        keys = np.asarray(keys, dtype=np.int32).reshape(-1, 3)
+        qc = [np.ascontiguousarray(qrows[:, c]) for c in range(3)]
+        kc = [np.ascontiguousarray(keys[:, c]) for c in range(3)]
+        dq = np.empty((qrows.shape[0], dd))
+        dk = np.empty((keys.shape[0], dd))
+        dv = np.empty((keys.shape[0], dd))
+        self.lib.orc_bwd_sel(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                             _ptr(ql), float(scale), qrows.shape[0], *[_ptr(x) for x in qc],
+                             _ptr(dq), keys.shape[0], *[_ptr(x) for x in kc], _ptr(dk),
+                             _ptr(dv))
+        return dq, dk, dv
 
     def chunk(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
               W: int, scale: float):
@@ -184,6 +223,14 @@ def fwd_rows(*a, **kw):
 
 def chunk(*a, **kw):
     return default().chunk(*a, **kw)
+
+
+def bwd(*a, **kw):
+    return default().bwd(*a, **kw)
+
+
+def bwd_sel(*a, **kw):
+    return default().bwd_sel(*a, **kw)
 
 
 def decode(*a, **kw):

@@ -459,3 +459,230 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the full-sequence forward, for a scalar loss whose gradient
+ * with respect to the output o is dout.  [M003 §07] asks that the Q/K/V
+ * gradients of the masked attention be checked by finite differences; this is
+ * the plain chain rule through s_ij = scale <q_i, k_j>, the softmax over the
+ * allowed keys and o_i = sum_j P_ij v_j:
+ *   dv_j  = sum_i P_ij dout_i
+ *   dP_ij = <dout_i, v_j>
+ *   D_i   = sum_j P_ij dP_ij              (softmax Jacobian: dS = P (dP - D))
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dq_i  = scale sum_j dS_ij k_j
+ *   dk_j  = scale sum_i dS_ij q_i
+ * with the sums over allowed (i, j) only.  READING: padded rows and keys (at or
+ * past q_len) get zero gradients, like their zero outputs.  Grouped heads: the
+ * key and value gradients of kv head g sum over its G query heads.
+ * The row values (log-sum-exp, D) are computed per row from its scores. */
+
+/* Log-sum-exp of row i's allowed scores and D_i = sum_j P_ij <dout_i, v_j>.
+ * Returns 0 (and leaves the outputs untouched) when the row sees no key. */
+static int row_stats(int d, int W, int len, double scale, const double *qi, int64_t i,
+                     const double *kb, const double *vb, const double *doi,
+                     double *lse, double *D)
+{
+    int64_t j;
+    int c, any = 0;
+    double m = -INFINITY, l = 0.0, dd = 0.0;
+    for (j = 0; j < len; j++) {
+        double s = 0.0;
+        if (!allowed(i, j, W))
+            continue;
+        for (c = 0; c < d; c++)
+            s += qi[c] * kb[j * d + c];
+        s *= scale;
+        if (!any || s > m)
+            m = s;
+        any = 1;
+    }
+    if (!any || i >= len)
+        return 0;
+    for (j = 0; j < len; j++) {
+        double s = 0.0;
+        if (!allowed(i, j, W))
+            continue;
+        for (c = 0; c < d; c++)
+            s += qi[c] * kb[j * d + c];
+        l += exp(s * scale - m);
+    }
+    *lse = m + log(l);
+    for (j = 0; j < len; j++) {
+        double s = 0.0, p, dp = 0.0;
+        if (!allowed(i, j, W))
+            continue;
+        for (c = 0; c < d; c++)
+            s += qi[c] * kb[j * d + c];
+        p = exp(s * scale - *lse);
+        for (c = 0; c < d; c++)
+            dp += doi[c] * vb[j * d + c];
+        dd += p * dp;
+    }
+    *D = dd;
+    return 1;
+}
+
+/* dq_i = scale sum_j P_ij (dP_ij - D_i) k_j over row i's allowed keys. */
+static void row_dq(int d, int W, int len, double scale, const double *qi, int64_t i,
+                   const double *kb, const double *vb, const double *doi, double lse,
+                   double D, double *dqi)
+{
+    int64_t j;
+    int c;
+    for (c = 0; c < d; c++)
+        dqi[c] = 0.0;
+    for (j = 0; j < len; j++) {
+        double s = 0.0, p, dp = 0.0, ds;
+        if (!allowed(i, j, W))
+            continue;
+        for (c = 0; c < d; c++)
+            s += qi[c] * kb[j * d + c];
+        p = exp(s * scale - lse);
+        for (c = 0; c < d; c++)
+            dp += doi[c] * vb[j * d + c];
+        ds = p * (dp - D);
+        for (c = 0; c < d; c++)
+            dqi[c] += scale * ds * kb[j * d + c];
+    }
+}
+
+/* dk_j, dv_j of key j of kv head g of sequence b: sums over the rows of every
+ * query head of the group that see key j.  lse/D: per-row values ([B][H][N]),
+ * valid where ok[] is set. */
+static void key_grad(int H, int G, int N, int d, int W, int len, double scale, int64_t b,
+                     int64_t g, int64_t j, const double *q, const double *kb,
+                     const double *vb, const double *dout, const double *lse,
+                     const double *Dv, const unsigned char *ok, double *dkj, double *dvj)
+{
+    int64_t h, i;
+    int c;
+    for (c = 0; c < d; c++) {
+        dkj[c] = 0.0;
+        dvj[c] = 0.0;
+    }
+    if (j >= len)
+        return;
+    for (h = g * G; h < (g + 1) * G; h++) {
+        for (i = 0; i < len; i++) {
+            const int64_t row = (b * H + h) * (int64_t)N + i;
+            const double *qi = q + row * d;
+            const double *doi = dout + row * d;
+            double s = 0.0, p, dp = 0.0, ds;
+            if (!allowed(i, j, W) || !ok[row])
+                continue;
+            for (c = 0; c < d; c++)
+                s += qi[c] * kb[j * d + c];
+            p = exp(s * scale - lse[row]);
+            for (c = 0; c < d; c++)
+                dp += doi[c] * vb[j * d + c];
+            ds = p * (dp - Dv[row]);
+            for (c = 0; c < d; c++) {
+                dvj[c] += p * doi[c];
+                dkj[c] += scale * ds * qi[c];
+            }
+        }
+    }
+}
+
+/* Full backward.  q, dout, dq: [B][H][N][d]; k, v, dk, dv: [B][Hkv][N][d];
+ * lse_out (may be NULL): [B][H][N] natural-log log-sum-exp of each row's
+ * allowed scores, -inf for rows that see no key. */
+void orc_bwd(int B, int H, int Hkv, int N, int d, int W, const double *q, const double *k,
+             const double *v, const double *dout, const int32_t *q_len, double scale,
+             double *dq, double *dk, double *dv, double *lse_out)
+{
+    const int G = H / Hkv;
+    const int64_t rows = (int64_t)B * H * N;
+    double *lse = malloc(sizeof(double) * (size_t)rows);
+    double *Dv = malloc(sizeof(double) * (size_t)rows);
+    unsigned char *ok = malloc((size_t)rows);
+    int64_t r, key;
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (r = 0; r < rows; r++) {
+        const int64_t b = r / ((int64_t)H * N), h = (r / N) % H, i = r % N;
+        const int len = q_len ? q_len[b] : N;
+        const int64_t g = h / G;
+        const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+        const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+        int c;
+        ok[r] = (unsigned char)row_stats(d, W, len, scale, q + r * d, i, kb, vb, dout + r * d,
+                                         &lse[r], &Dv[r]);
+        if (ok[r])
+            row_dq(d, W, len, scale, q + r * d, i, kb, vb, dout + r * d, lse[r], Dv[r],
+                   dq + r * d);
+        else
+            for (c = 0; c < d; c++)
+                dq[r * d + c] = 0.0;
+        if (lse_out)
+            lse_out[r] = ok[r] ? lse[r] : -INFINITY;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (key = 0; key < (int64_t)B * Hkv * N; key++) {
+        const int64_t b = key / ((int64_t)Hkv * N), g = (key / N) % Hkv, j = key % N;
+        const int len = q_len ? q_len[b] : N;
+        const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+        const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+        key_grad(H, G, N, d, W, len, scale, b, g, j, q, kb, vb, dout, lse, Dv, ok,
+                 dk + key * d, dv + key * d);
+    }
+    free(lse); free(Dv); free(ok);
+}
+
+/* The same gradients for selected entries only (large inputs): dq of rows
+ * (qb, qh, qi)[r] and dk, dv of keys (kb_, kg, kj)[r].  Row values are
+ * computed for exactly the rows each selection needs. */
+void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
+                 const double *k, const double *v, const double *dout, const int32_t *q_len,
+                 double scale, int nq_sel, const int32_t *qb, const int32_t *qh,
+                 const int32_t *qi, double *dq_rows, int nk_sel, const int32_t *kb_,
+                 const int32_t *kg, const int32_t *kj, double *dk_rows, double *dv_rows)
+{
+    const int G = H / Hkv;
+    int r;
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < nq_sel; r++) {
+        const int64_t b = qb[r], h = qh[r], i = qi[r], g = h / G;
+        const int len = q_len ? q_len[b] : N;
+        const int64_t row = (b * H + h) * (int64_t)N + i;
+        const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+        const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+        double lse, D;
+        int c;
+        if (row_stats(d, W, len, scale, q + row * d, i, kb, vb, dout + row * d, &lse, &D))
+            row_dq(d, W, len, scale, q + row * d, i, kb, vb, dout + row * d, lse, D,
+                   dq_rows + (int64_t)r * d);
+        else
+            for (c = 0; c < d; c++)
+                dq_rows[(int64_t)r * d + c] = 0.0;
+    }
+    for (r = 0; r < nk_sel; r++) {
+        const int64_t b = kb_[r], g = kg[r], j = kj[r];
+        const int len = q_len ? q_len[b] : N;
+        const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
+        const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
+        /* row values of every row that sees key j */
+        double *lse = calloc((size_t)H * N, sizeof(double));
+        double *Dv = calloc((size_t)H * N, sizeof(double));
+        unsigned char *ok = calloc((size_t)H * N, 1);
+        int64_t h;
+        for (h = g * G; h < (g + 1) * G; h++) {
+            int64_t i;
+            const int64_t iend = (j + W < N) ? j + W : N;
+#pragma omp parallel for schedule(dynamic, 4)
+            for (i = j; i < iend; i++) {
+                const int64_t row = (b * H + h) * (int64_t)N + i;
+                ok[h * N + i] = (unsigned char)row_stats(d, W, len, scale, q + row * d, i, kb,
+                                                         vb, dout + row * d, &lse[h * N + i],
+                                                         &Dv[h * N + i]);
+            }
+        }
+        /* key_grad indexes row values as [b][h][i]; view this sequence's slice */
+        key_grad(H, G, N, d, W, len, scale, 0, g, j, q + b * (int64_t)H * N * d, kb, vb,
+                 dout + b * (int64_t)H * N * d, lse, Dv, ok, dk_rows + (int64_t)r * d,
+                 dv_rows + (int64_t)r * d);
+        free(lse); free(Dv); free(ok);
+    }
+}

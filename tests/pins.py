@@ -506,6 +506,107 @@ def pin_decode_rotation_invariance(O):
         assert np.array_equal(np.roll(got[1], -shift, axis=2), base[1])
 
 
+# ---------------------------------------------------------------------------
+# Gradients ([M003] §07: Q/K/V gradients of the masked attention are checked by
+# finite differences; §08: outputs and gradients, boundaries, valid lengths).
+
+def _bwd_case(seed, B=2, H=4, Hkv=2, N=13, d=5):
+    rng = _rng(seed)
+    return (rng.standard_normal((B, H, N, d)), rng.standard_normal((B, Hkv, N, d)),
+            rng.standard_normal((B, Hkv, N, d)), rng.standard_normal((B, H, N, d)), rng)
+
+
+def pin_bwd_finite_differences(O):
+    """Directional derivatives of L = <o(q, k, v), dout> by central differences
+    of the forward equal <grad, direction> for q, k and v, with grouped heads,
+    padded sequences and windows shorter than, inside and beyond the length."""
+    for seed, W, ql in ((40, 3, [13, 8]), (41, 1, [13, 13]), (42, 20, [9, 13]),
+                        (43, 6, [1, 12])):
+        q, k, v, do, rng = _bwd_case(seed)
+        sc = 0.6
+        dq, dk, dv, _ = O.bwd(q, k, v, do, W=W, scale=sc, q_len=ql)
+        eps = 1e-5
+
+        def loss(q_, k_, v_):
+            return float((O.fwd(q_, k_, v_, W=W, scale=sc, q_len=ql) * do).sum())
+
+        for name, g in (("q", dq), ("k", dk), ("v", dv)):
+            x = {"q": q, "k": k, "v": v}
+            e = rng.standard_normal(x[name].shape)
+            xp, xm = dict(x), dict(x)
+            xp[name] = x[name] + eps * e
+            xm[name] = x[name] - eps * e
+            fd = (loss(xp["q"], xp["k"], xp["v"]) - loss(xm["q"], xm["k"], xm["v"])) / (2 * eps)
+            an = float((g * e).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (seed, name, fd, an)
+
+
+def pin_bwd_window_mask_autograd(O):
+    """Gradients and row log-sum-exp equal torch autograd through SDPA with the
+    band mask of library triangles (fp64, grouped heads by repeat)."""
+    rng = _rng(44)
+    B, H, Hkv, N, d = 1, 6, 2, 33, 8
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, H, N, d))
+    sc = 1.0 / math.sqrt(d)
+    for W in (1, 4, 17, 40):
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        G = H // Hkv
+        mask = torch.from_numpy(_band_mask(N, N, W))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), attn_mask=mask,
+            scale=sc)
+        out.backward(torch.from_numpy(do))
+        dq, dk, dv, lse = O.bwd(q, k, v, do, W=W, scale=sc)
+        for got, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+            assert np.max(np.abs(got - ref.numpy())) <= 1e-12, W
+        scores = (torch.from_numpy(q) @ torch.from_numpy(k).repeat_interleave(G, dim=1)
+                  .transpose(-1, -2)) * sc
+        ref_lse = torch.logsumexp(scores.masked_fill(~mask, -math.inf), dim=-1)
+        assert np.max(np.abs(lse - ref_lse.numpy())) <= 1e-12, W
+
+
+def pin_bwd_closed_forms(O):
+    """Sum over keys of dk is 0 (each row's dS sums to 0); sum over keys of dv
+    equals the sum of dout over the group's valid rows (each row's P sums to
+    1); equal keys give dq = 0; padded rows and keys get zero gradients and
+    padded rows a log-sum-exp of -inf."""
+    q, k, v, do, rng = _bwd_case(45, N=15)
+    ql = [15, 6]
+    W = 4
+    dq, dk, dv, lse = O.bwd(q, k, v, do, W=W, scale=0.8, q_len=ql)
+    G = q.shape[1] // k.shape[1]
+    for b in range(2):
+        L = ql[b]
+        for g in range(k.shape[1]):
+            assert np.max(np.abs(dk[b, g].sum(axis=0))) <= 1e-12
+            want = do[b, g * G:(g + 1) * G, :L].sum(axis=(0, 1))
+            assert np.max(np.abs(dv[b, g].sum(axis=0) - want)) <= 1e-12
+        assert np.all(dq[b, :, L:] == 0) and np.all(dk[b, :, L:] == 0)
+        assert np.all(dv[b, :, L:] == 0) and np.all(np.isneginf(lse[b, :, L:]))
+        assert np.all(np.isfinite(lse[b, :, :L]))
+    kc = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    dq2, _, _, _ = O.bwd(q, kc, v, do, W=W, scale=0.8, q_len=ql)
+    assert np.max(np.abs(dq2)) <= 1e-12
+
+
+def pin_bwd_selection_matches(O):
+    """The selected-entry gradients equal the corresponding full gradients."""
+    q, k, v, do, rng = _bwd_case(46, N=17)
+    ql = [17, 11]
+    W = 5
+    dq, dk, dv, _ = O.bwd(q, k, v, do, W=W, scale=0.5, q_len=ql)
+    qrows = [[0, 0, 0], [1, 3, 10], [1, 2, 16], [0, 1, 9]]
+    keys = [[0, 1, 0], [1, 0, 10], [1, 1, 16], [0, 0, 12]]
+    sq, sk, sv = O.bwd_sel(q, k, v, do, W=W, scale=0.5, qrows=qrows, keys=keys, q_len=ql)
+    for r, (b, h, i) in enumerate(qrows):
+        assert np.array_equal(sq[r], dq[b, h, i])
+    for r, (b, g, j) in enumerate(keys):
+        assert np.array_equal(sk[r], dk[b, g, j]) and np.array_equal(sv[r], dv[b, g, j])
+
+
 PINS = [
     pin_window_visible_sets,
     pin_pair_counts,
@@ -524,4 +625,8 @@ PINS = [
     pin_chunk_union,
     pin_decode_against_full_sequence,
     pin_decode_rotation_invariance,
+    pin_bwd_finite_differences,
+    pin_bwd_window_mask_autograd,
+    pin_bwd_closed_forms,
+    pin_bwd_selection_matches,
 ]

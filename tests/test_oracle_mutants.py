@@ -37,6 +37,15 @@ MUTANTS = {
                               "const int64_t area = (int64_t)tile_q * tile_k;"),
     "ring_slot_position_shift": ("kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r;",
                                  "kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r + 1;"),
+    "bwd_row_D_dropped": ("ds = p * (dp - D);", "ds = p * dp;"),
+    "bwd_key_D_dropped": ("ds = p * (dp - Dv[row]);", "ds = p * dp;"),
+    "bwd_dk_scale_dropped": ("dkj[c] += scale * ds * qi[c];", "dkj[c] += ds * qi[c];"),
+    "bwd_dv_uses_ds": ("dvj[c] += p * doi[c];", "dvj[c] += ds * doi[c];"),
+    "bwd_dq_uses_v": ("dqi[c] += scale * ds * kb[j * d + c];",
+                      "dqi[c] += scale * ds * vb[j * d + c];"),
+    "bwd_lse_no_log": ("*lse = m + log(l);", "*lse = m + l;"),
+    "bwd_group_first_head_only": ("for (h = g * G; h < (g + 1) * G; h++) {",
+                                  "for (h = g * G; h < g * G + 1; h++) {"),
     "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
                           "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
 }
