@@ -9,7 +9,9 @@ Functions keep the ABI's names:
 
     swa_blockmask_size(B, nq, nk, tile_q, tile_k)          -> (cls_elems, max_nnz)
     swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, ...) -> dict (host numpy)
-    swa_fwd(q, k, v, o, W, meta, tile_q, tile_k, q_len=None, scale=None)
+    swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None)
+    swa_bwd_workspace_size(B, H, N)
+    swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, scale=None)
     swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len,
                       next_pos, o, W, meta, tile_q, tile_k, scale=None)
     swa_decode_workspace_size(B, H, d, W)
@@ -39,7 +41,8 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 
 # Symbols declared in include/swa.h (checked by the CPU tests).
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
-           "swa_decode_workspace_size", "swa_decode", "swa_last_error")
+           "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
+           "swa_last_error")
 
 
 class SwaError(RuntimeError):
@@ -70,7 +73,11 @@ def lib():
                                              ctypes.POINTER(ctypes.c_size_t)]
             L.swa_blockmask_build.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P,
                                               P, P, P, P, ctypes.POINTER(MaskStats)]
-            L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, F, P]
+            L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, P]
+            L.swa_bwd_workspace_size.argtypes = [I, I, I]
+            L.swa_bwd_workspace_size.restype = ctypes.c_size_t
+            L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                  P, ctypes.c_size_t, F, P]
             L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
                                             P, P, P, P, F, P]
             L.swa_decode_workspace_size.argtypes = [I, I, I, I]
@@ -80,7 +87,7 @@ def lib():
             L.swa_last_error.argtypes = []
             L.swa_last_error.restype = ctypes.c_char_p
             for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
-                      "swa_prefill_chunk", "swa_decode"):
+                      "swa_prefill_chunk", "swa_decode", "swa_bwd"):
                 getattr(L, n).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -149,6 +156,7 @@ def meta_to_device(meta, device):
     return {"row_ptr": torch.from_numpy(meta["row_ptr"]).to(dev),
             "col": torch.from_numpy(col).to(dev),
             "col_cls": torch.from_numpy(ccls).to(dev),
+            "cls": torch.from_numpy(np.ascontiguousarray(meta["cls"]).reshape(-1)).to(dev),
             "tile_q": meta["tile_q"], "tile_k": meta["tile_k"]}
 
 
@@ -177,8 +185,9 @@ def _require(cond, msg):
         raise SwaError(SWA_EINVAL, msg)
 
 
-def swa_fwd(q, k, v, o, W, meta, q_len=None, scale=None, stream=None):
-    """Full-sequence forward.  q,o [B,H,N,d], k,v [B,Hkv,N,d] device tensors."""
+def swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None, stream=None):
+    """Full-sequence forward.  q,o [B,H,N,d], k,v [B,Hkv,N,d] device tensors;
+    lse: optional fp32 [B,H,N] device tensor for the row log-sum-exp."""
     for t in (q, k, v, o):
         _require(t.is_contiguous(), "tensors must be contiguous")
     B, H, N, d = q.shape
@@ -190,8 +199,37 @@ def swa_fwd(q, k, v, o, W, meta, q_len=None, scale=None, stream=None):
     _check(lib().swa_fwd(_dtype_code(q), B, H, Hkv, N, d, W, meta["tile_q"], meta["tile_k"],
                          _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(q_len),
                          _dptr(meta["row_ptr"]), _dptr(meta["col"]), _dptr(meta["col_cls"]),
-                         ctypes.c_float(scale), _stream(q, stream)))
+                         _dptr(lse), ctypes.c_float(scale), _stream(q, stream)))
     return o
+
+
+def swa_bwd_workspace_size(B, H, N) -> int:
+    return int(lib().swa_bwd_workspace_size(B, H, N))
+
+
+def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, scale=None,
+            stream=None):
+    """Gradients of swa_fwd for output gradient dout.  q,o,dout,dq [B,H,N,d];
+    k,v,dk,dv [B,Hkv,N,d]; lse fp32 [B,H,N] from swa_fwd; workspace: device
+    tensor of at least swa_bwd_workspace_size(B, H, N) bytes."""
+    for t in (q, k, v, o, dout, lse, dq, dk, dv):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (B, Hkv, N, d) and tuple(v.shape) == (B, Hkv, N, d) and
+             tuple(o.shape) == (B, H, N, d) and tuple(dout.shape) == (B, H, N, d) and
+             tuple(dq.shape) == (B, H, N, d) and tuple(dk.shape) == (B, Hkv, N, d) and
+             tuple(dv.shape) == (B, Hkv, N, d) and tuple(lse.shape) == (B, H, N),
+             "shape mismatch")
+    _require(len({t.dtype for t in (q, k, v, o, dout, dq, dk, dv)}) == 1, "dtype mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().swa_bwd(_dtype_code(q), B, H, Hkv, N, d, W, meta["tile_q"], meta["tile_k"],
+                         _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(dout), _dptr(lse),
+                         _dptr(q_len), _dptr(meta["row_ptr"]), _dptr(meta["col"]),
+                         _dptr(meta["cls"]), _dptr(dq), _dptr(dk), _dptr(dv), _dptr(workspace),
+                         ctypes.c_size_t(ws_bytes), ctypes.c_float(scale), _stream(q, stream)))
+    return dq, dk, dv
 
 
 def swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,

@@ -84,8 +84,8 @@ extern "C" const char *swa_last_error(void) { return swa::g_err; }
 extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q,
                        int tile_k, const void *q, const void *k, const void *v, void *o,
                        const int32_t *q_len_dev, const int32_t *row_ptr_dev,
-                       const int32_t *col_dev, const uint8_t *col_cls_dev, float scale,
-                       void *stream) {
+                       const int32_t *col_dev, const uint8_t *col_cls_dev, float *lse_dev,
+                       float scale, void *stream) {
     static const char *fn = "swa_fwd";
     swa::clear_error();
     int rc;
@@ -108,9 +108,55 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     a.q = q; a.k = k; a.v = v; a.o = o;
     a.q_len = q_len_dev;
     a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.lse = lse_dev;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
+}
+
+extern "C" size_t swa_bwd_workspace_size(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return (size_t)B * H * N * sizeof(float);
+}
+
+extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q,
+                       int tile_k, const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse_dev, const int32_t *q_len_dev,
+                       const int32_t *row_ptr_dev, const int32_t *col_dev,
+                       const uint8_t *cls_dev, void *dq, void *dk, void *dv, void *workspace,
+                       size_t ws_bytes, float scale, void *stream) {
+    static const char *fn = "swa_bwd";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (N < 1) return fail(SWA_EINVAL, "%s: N=%d must be >= 1", fn, N);
+    if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    if (tile_q < 1 || tile_k < 1)
+        return fail(SWA_EINVAL, "%s: tiles must be positive (tile_q=%d tile_k=%d)", fn, tile_q,
+                    tile_k);
+    const void *ptrs[] = {q, k, v, o, dout, lse_dev, dq, dk, dv, workspace, row_ptr_dev, col_dev};
+    const char *names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace",
+                           "row_ptr", "col"};
+    if ((rc = check_ptrs(fn, ptrs, names, 12))) return rc;
+    if (!cls_dev) return fail(SWA_EINVAL, "%s: cls is NULL", fn);
+    if (ws_bytes < swa_bwd_workspace_size(B, H, N))
+        return fail(SWA_EINVAL, "%s: workspace of %zu bytes is below the %zu required", fn,
+                    ws_bytes, swa_bwd_workspace_size(B, H, N));
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+
+    swa::BwdArgs a = {};
+    a.B = B; a.H = H; a.Hkv = Hkv; a.N = N; a.d = d; a.W = W;
+    a.tile_q = tile_q; a.tile_k = tile_k;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse_dev;
+    a.q_len = q_len_dev;
+    a.row_ptr = row_ptr_dev; a.col = col_dev; a.cls = cls_dev;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dvec = (float *)workspace;
+    a.scale = scale;
+    a.bf16 = dt == SWA_BF16;
+    return launched(fn, swa::launch_bwd(a, (hipStream_t)stream));
 }
 
 extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,

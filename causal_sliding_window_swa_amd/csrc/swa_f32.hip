@@ -42,6 +42,7 @@ struct RowState {
             if (c < d) o[c] = fmaf(p, vrow[c], o[c] * corr);
         m = m2;
     }
+    __device__ float lse() const { return (l > 0.f) ? m + logf(l) : -INFINITY; }
     __device__ void store(float *orow, int d) const {
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
             }
         }
         st.store(orow, d);
+        if (MODE == 0 && a.lse) a.lse[((size_t)b * a.H + h) * nq + i] = st.lse();
     }
 }
 

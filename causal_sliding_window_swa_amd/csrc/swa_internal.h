@@ -26,6 +26,7 @@ struct AttnArgs {
     const int32_t *ring_start, *cache_len, *next_pos;
     const int32_t *row_ptr, *col;
     const uint8_t *col_cls;
+    float *lse;  // mode 0, may be null: [B][H][nq] natural-log row log-sum-exp
     float scale;
 };
 
@@ -56,6 +57,21 @@ hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 int decode_bf16_splits(int B, int Hkv, int W);
 int decode_max_splits(int W);
+// Backward of the full-sequence forward (swa_bwd.hip).
+struct BwdArgs {
+    int B, H, Hkv, N, d, W, tile_q, tile_k;
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    const int32_t *q_len;
+    const int32_t *row_ptr, *col;
+    const uint8_t *cls;  // [B][nqt][nkt] class grid
+    void *dq, *dk, *dv;
+    float *dvec;  // workspace: [B][H][N] fp32 row values D = <dout, o>
+    float scale;
+    int bf16;
+};
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
+
 // Ring bookkeeping (swa_ring.hip): write the new rows into their slots, then
 // advance the state; launch_commit does both (after a chunk's attention).
 hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s);

@@ -406,9 +406,14 @@ void tile_kernel(AttnArgs a) {
         if (e + 1 < e1) tile(e + 1, stage1, stage0);
     }
 
-    // ---- epilogue: O = O / l; rows without any visible key (padding) get 0
+    // ---- epilogue: O = O / l; rows without any visible key (padding) get 0.
+    // The row log-sum-exp (natural log) of the scaled scores is
+    // (m_ref + log2 l) * ln 2, since l = sum exp2(s*c2 - m_ref).
     if (myrow < nq) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        if (MODE == 0 && a.lse && hh == 0)
+            a.lse[((size_t)b * a.H + h) * nq + myrow] =
+                (l_run > 0.f) ? (m_ref + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
         __bf16 *op = (__bf16 *)a.o + (((size_t)b * a.H + h) * nq + myrow) * D;
 #pragma unroll
         for (int db = 0; db < DB; db++)

@@ -64,6 +64,19 @@ def gen_fwd(B, H, Hkv, N, d, seed, std=0.5, dtype="bf16", len_lo=None, len_hi=No
     return dict(q=q, k=k, v=v, q_len=q_len)
 
 
+def gen_bwd(B, H, Hkv, N, d, seed, std=0.5, dtype="bf16", len_lo=None, len_hi=None):
+    """The forward inputs of gen_fwd (same seed gives the same q, k, v, q_len)
+    plus an output gradient dout [B,H,N,d] drawn after them, zero on padded rows."""
+    inp = gen_fwd(B, H, Hkv, N, d, seed, std, dtype, len_lo, len_hi)
+    gen = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    dout = _randn(gen, (B, H, N, d), std, dtype)
+    if inp["q_len"] is not None:
+        for b in range(B):
+            dout[b, :, int(inp["q_len"][b]):] = 0
+    inp["dout"] = dout
+    return inp
+
+
 def gen_chunk(B, H, Hkv, Tq, W, d, seed, std=0.5, dtype="bf16", p_lo=None, p_hi=None,
               p=None):
     """A chunk of Tq new tokens per request plus a full ring cache of W slots.

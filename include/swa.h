@@ -117,12 +117,43 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k
  * Supported: SWA_BF16 with d in {64, 128}, (tile_q, tile_k) = (128, 64) or
  * (64, 64); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
  * W >= N is legal (dense causal).
+ * lse_dev: NULL, or device fp32 [B][H][N] that receives each row's natural-log
+ * log-sum-exp of its visible scaled scores (-inf for rows that see no key),
+ * which swa_bwd needs.
  * Errors: SWA_EINVAL (W < 1, H % Hkv != 0, N < 1, NULL or misaligned
  * pointers), SWA_EUNSUPPORTED, SWA_EHIP. */
 int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q, int tile_k,
             const void *q, const void *k, const void *v, void *o,
             const int32_t *q_len_dev,
             const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *col_cls_dev,
+            float *lse_dev, float scale, void *stream);
+
+/* Bytes of device workspace swa_bwd needs (fp32 row values [B][H][N]);
+ * 0 for non-positive sizes. */
+size_t swa_bwd_workspace_size(int B, int H, int N);
+
+/* Gradients of swa_fwd [M003 §07 asks for the Q/K/V gradients of the masked
+ * attention, checked by finite differences].  For output gradient dout, with
+ * P the softmax of s = scale q.k over each row's visible keys and o = P v:
+ *   D_i = <dout_i, o_i>, dS_ij = P_ij (<dout_i, v_j> - D_i),
+ *   dq_i = scale sum_j dS_ij k_j, dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i P_ij dout_i  (visible pairs only; grouped heads summed).
+ * q, o, dout, dq [B][H][N][d]; k, v, dk, dv [B][Hkv][N][d], all of dtype dt
+ * (fp32 arithmetic inside); lse_dev: the fp32 [B][H][N] that swa_fwd wrote
+ * for this q, k, v; q_len_dev as for swa_fwd.  row_ptr_dev / col_dev: the
+ * block metadata of swa_fwd (query rows visit their tile's key tiles);
+ * cls_dev: its class grid [B][nqt][nkt] (keys visit the query tiles whose
+ * entry for their key tile is live).  Padded rows and keys get 0.  The
+ * caller owns every buffer, including workspace (ws_bytes >=
+ * swa_bwd_workspace_size(B, H, N)); the outputs are overwritten, not summed.
+ * Supported: as swa_fwd for d; any positive tiles matching the metadata.
+ * Errors: SWA_EINVAL (as swa_fwd, small workspace), SWA_EUNSUPPORTED,
+ * SWA_EHIP. */
+int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q, int tile_k,
+            const void *q, const void *k, const void *v, const void *o, const void *dout,
+            const float *lse_dev, const int32_t *q_len_dev,
+            const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *cls_dev,
+            void *dq, void *dk, void *dv, void *workspace, size_t ws_bytes,
             float scale, void *stream);
 
 /* Chunked prefill of Tq new tokens against a ring-buffer cache [Ch10 §10.2],

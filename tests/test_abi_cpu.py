@@ -53,7 +53,7 @@ P = ctypes.c_void_p
 def _fwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, tq=128, tk=64, ptr=16):
     p = ctypes.c_void_p(ptr)
     return swa.lib().swa_fwd(dt, B, H, Hkv, N, d, W, tq, tk, p, p, p, p, None, p, p, p,
-                             ctypes.c_float(0.1), None)
+                             None, ctypes.c_float(0.1), None)
 
 
 def test_fwd_validation_codes():
@@ -68,6 +68,30 @@ def test_fwd_validation_codes():
     assert _fwd(ptr=8) == swa.SWA_EINVAL  # misaligned
     assert _fwd(dt=7) == swa.SWA_EINVAL
     assert "window" in swa.swa_last_error() or True
+
+
+def _bwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, ptr=16, ws=None, cls=True):
+    p = ctypes.c_void_p(ptr)
+    need = swa.swa_bwd_workspace_size(B, H, N)
+    wsb = need if ws is None else ws
+    return swa.lib().swa_bwd(dt, B, H, Hkv, N, d, W, 128, 64, p, p, p, p, p, p, None, p, p,
+                             p if cls else None, p, p, p, p, ctypes.c_size_t(wsb),
+                             ctypes.c_float(0.1), None)
+
+
+def test_bwd_validation_codes():
+    assert swa.swa_bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 4
+    assert swa.swa_bwd_workspace_size(0, 3, 5) == 0
+    assert _bwd(W=0) == swa.SWA_EINVAL
+    assert _bwd(H=3, Hkv=2) == swa.SWA_EINVAL
+    assert _bwd(N=0) == swa.SWA_EINVAL
+    assert _bwd(d=96) == swa.SWA_EUNSUPPORTED
+    assert _bwd(dt=1, d=6) == swa.SWA_EUNSUPPORTED
+    assert _bwd(ptr=0) == swa.SWA_EINVAL
+    assert _bwd(ptr=8) == swa.SWA_EINVAL
+    assert _bwd(ws=100) == swa.SWA_EINVAL
+    assert "workspace" in swa.swa_last_error()
+    assert _bwd(cls=False) == swa.SWA_EINVAL
 
 
 def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False):
