@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list: prefill,gqa,chunk,decode")
+    ap.add_argument("--only", default="", help="comma list: prefill,gqa,chunk,decode,bwd")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(scale for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -76,7 +76,8 @@ def main():
     import causal_sliding_window_swa_amd as swa
     from causal_sliding_window_swa_amd import synth
 
-    only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode"}
+    only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode",
+                                                         "bwd"}
     dev = torch.device("cuda:0")
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -148,6 +149,21 @@ def main():
     prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, flops=flops, meta_ms=t_meta,
                    meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
     out["prefill"] = prefill
+
+    # ---------------- backward on the prefill workload -------------
+    if "bwd" in only:
+        gen = torch.Generator(device="cpu").manual_seed(1 + 7919)
+        dout = (torch.randn(q.shape, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        swa.swa_fwd(q, k, v, o, W, md, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wsb = torch.empty(swa.swa_bwd_workspace_size(B, H, N) // 4, dtype=torch.float32,
+                          device=dev)
+        fb = lambda: swa.swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, wsb, W, md)
+        wb, eb = timed(fb, max(3, K // 10), 1)
+        out["bwd"] = dict(wall_ms=wb, kernel_ms=eb, flops=2.5 * flops)
+        log("bwd: wall %.3f ms, event %.3f ms" % (wb, eb))
+        del dout, lse, dq, dk, dv, wsb
     del inp
 
     # ---------------- GQA prefill with per-sequence lengths -------------
@@ -290,6 +306,14 @@ def main():
                                            "swa_decode", src_digest("swa_decode_bf16.hip")),
                                        "kernel_ms": round(dd["kernel_ms"], 5),
                                        "kernels": "split + combine"}}
+    if "bwd" in out:
+        bb = out["bwd"]
+        t = bb["flops"] / (bb["wall_ms"] * 1e-3) / 1e12
+        line["backward"] = {"workload": "backward of the prefill workload (dq, dk, dv), "
+                                        "useful FLOPs = 2.5 x forward = 10 d (visible pairs)",
+                            "TFLOP_per_s": round(t, 2),
+                            "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                            "ms_per_step": round(bb["wall_ms"], 4)}
     if "gqa" in out:
         g3 = out["gqa"]
         t = g3["flops"] / (g3["wall_ms"] * 1e-3) / 1e12

@@ -206,7 +206,16 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
-    return a.bf16 ? launch_t<__bf16>(a, s) : launch_t<float>(a, s);
+    if (!a.bf16) return launch_t<float>(a, s);
+    if (!bwd_bf16_supported(a)) return launch_t<__bf16>(a, s);
+    // row values D on this path, then the MFMA kernels
+    const long rows = (long)a.B * a.H * a.N;
+    if ((rows + 3) / 4 > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dvec_kernel<__bf16>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_bwd_bf16(a, s);
 }
 
 }  // namespace swa

@@ -1,0 +1,445 @@
+// swa_bwd_bf16.hip -- bf16 MFMA kernels for the gradients of the full-sequence
+// sliding-window forward (d in {64, 128}, tile_k = 64).  Same quantities as
+// swa_bwd.hip ("Weight sparsity vs attention sparsity" §07); with the row
+// log-sum-exp of the forward, P = exp(s - lse) <= 1, so no running max is
+// needed.  Fragment layouts of v_mfma_f32_32x32x16_bf16 as in the forward:
+// A lane l = A[l%32][(l/32)*8 .. +8], B lane l = B[(l/32)*8 .. +8][l%32],
+// C element 4i+j of lane l = C[8i + 4(l/32) + j][l%32].
+//
+// dq_kernel: one workgroup per (query tile, head, request), 32 query rows per
+// wave, visiting the key tiles of its metadata row (K and V tiles staged in
+// LDS, double-buffered).  Per tile: S^T = K Q^T and dP^T = V dO^T (A = K or
+// V rows read from LDS, B = the wave's Q or dO rows in registers), then
+// dS^T = P^T (dP^T - D) and dQ^T += K^T dS^T with K^T read by transposing
+// LDS reads.  Each lane holds one query column: lse and D are per lane.
+//
+// dkdv_kernel: one workgroup per (key tile of 64, kv head, request), 32 keys
+// per wave held in registers, visiting 64-row steps of every query head of
+// the group in the query tiles whose class-grid entry for the key tile is
+// live (Q, dO, lse and D rows staged in LDS, double-buffered).  Per 32-row
+// block: S = Q K^T and dP = dO V^T (A = Q or dO rows from LDS, B = the wave's
+// K or V rows), P and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T
+// and Q^T read by transposing LDS reads.  Each lane holds one key column.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int BN = 64;  // keys per key tile; rows per dkdv step
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+
+// Workgroup p of T runs logical item L: XCD x = p % 8 gets a contiguous range.
+__device__ __forceinline__ int xcd_remap(int p, int T) {
+    const int x = p & 7, i = p >> 3, q = T >> 3, r = T & 7;
+    return x * q + (x < r ? x : r) + i;
+}
+
+// 16-byte chunk c of row r sits at physical chunk c ^ (r % chunks per row).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    return r & (CPR - 1);
+}
+
+// 8 bf16 of a transposing read pair: lanes' 4-element pieces of rows
+// kk*16 + 8r + tr_row, columns db*32 + tr_col .. +3 of a row-major tile.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char *base, int kk, int db, int tr_row,
+                                          int tr_col) {
+    constexpr int ROWB = D * 2, CPR = D / 8;
+    i16x4 v2[2];
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        const int row = kk * 16 + 8 * r + tr_row;
+        const int col = db * 32 + tr_col;
+        const int c = (col >> 3) ^ swz<CPR>(row);
+        v2[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(base + row * ROWB + c * 16 + (col & 7) * 2));
+    }
+    const u32x2 lo = __builtin_bit_cast(u32x2, v2[0]);
+    const u32x2 hi = __builtin_bit_cast(u32x2, v2[1]);
+    const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8, vv);
+}
+
+// A fragment of rows r0 .. r0+31 (lane row r0 + lq), k-step ks of a row-major tile.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char *base, int r0, int lq, int hh, int ks) {
+    constexpr int ROWB = D * 2, CPR = D / 8;
+    const int r = r0 + lq;
+    const int c = (2 * ks + hh) ^ swz<CPR>(r);
+    return __builtin_bit_cast(bf16x8, *(const u32x4 *)(base + r * ROWB + c * 16));
+}
+
+// Copy 64 rows x D of a row-major bf16 matrix (rows row0.., clamped to
+// rows < nrows) into an LDS tile, swizzled; NW waves share the work.
+template <int D, int NW>
+__device__ __forceinline__ void stage_rows(const __bf16 *src, int row0, int nrows, char *dst,
+                                           int wave, int lane) {
+    constexpr int ROWB = D * 2, CPR = D / 8, RPL = 64 / CPR, LPW = BN / RPL / NW;
+#pragma unroll
+    for (int i = 0; i < LPW; i++) {
+        const int ins = wave * LPW + i;
+        const int r = ins * RPL + lane / CPR;
+        const int pch = lane % CPR;
+        const int rr = min(row0 + r, nrows - 1);  // rows past the data: a real row, masked
+        const char *s = (const char *)(src + (size_t)rr * D) + (pch ^ swz<CPR>(r)) * 16;
+        __builtin_amdgcn_global_load_lds((const void *)s, (void *)(dst + ins * 1024), 16, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+void dq_kernel(BwdArgs a) {
+    constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
+    __shared__ __attribute__((aligned(1024))) char stage0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char stage1[2 * TILEB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hh = lane >> 5;
+    const int N = a.N;
+    const int nqt = (N + 32 * NW - 1) / (32 * NW);
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = a.H / a.Hkv;
+    const int h_in = L % G, qt = (L / G) % nqt, g = (L / (G * nqt)) % a.Hkv;
+    const int b = L / (G * nqt * a.Hkv);
+    const int h = g * G + h_in;
+    const int qlen = a.q_len ? a.q_len[b] : N;
+
+    const int myrow = qt * 32 * NW + wave * 32 + lq;
+    const bool qvalid = myrow < qlen;
+    const size_t rowidx = ((size_t)b * a.H + h) * N + myrow;
+    bf16x8 qf[KS], dof[KS];
+    {
+        const __bf16 *qp = (const __bf16 *)a.q + rowidx * D;
+        const __bf16 *dp = (const __bf16 *)a.dout + rowidx * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 z = {0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(qp + ks * 16 + hh * 8) : z);
+            dof[ks] = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(dp + ks * 16 + hh * 8) : z);
+        }
+    }
+    const float c2 = a.scale * LOG2E;
+    const float lse2 = qvalid ? a.lse[rowidx] * LOG2E : 0.f;
+    const float Dr = qvalid ? a.dvec[rowidx] : 0.f;
+
+    const size_t kvh = (size_t)b * a.Hkv + g;
+    const __bf16 *kb = (const __bf16 *)a.k + kvh * (size_t)N * D;
+    const __bf16 *vb = (const __bf16 *)a.v + kvh * (size_t)N * D;
+    auto issue = [&](int kt, char *dst) {
+        stage_rows<D, NW>(kb, kt * BN, N, dst, wave, lane);
+        stage_rows<D, NW>(vb, kt * BN, N, dst + TILEB, wave, lane);
+    };
+
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) dqacc[db][e] = 0.f;
+
+    const int e0 = a.row_ptr[b * nqt + qt], e1 = a.row_ptr[b * nqt + qt + 1];
+    const int tr_j = lane & 15;
+    const int tr_row = 4 * hh + (tr_j >> 2);
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);
+
+    auto tile = [&](int e, const char *cur, char *nxt) {
+        const int kt = a.col[e];
+        __syncthreads();
+        if (e + 1 < e1) issue(a.col[e + 1], nxt);
+        const char *ksm = cur;
+        const char *vsm = cur + TILEB;
+        // visible keys of this lane's row inside the tile: [a1, b1] (tile-local)
+        const int base = kt * BN;
+        int a1 = myrow - a.W + 1 - base, b1 = min(myrow, qlen - 1) - base;
+        if (!qvalid) b1 = -1;
+        a1 = max(a1, 0);
+        b1 = min(b1, BN - 1);
+        const bool empty = b1 < a1;
+        const int L1 = empty ? -(1 << 20) : a1 - 4 * hh;
+        const uint32_t n1 = empty ? 0u : (uint32_t)(b1 - a1);
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; kb2++)
+#pragma unroll
+            for (int e2 = 0; e2 < 16; e2++) {
+                s[kb2][e2] = 0.f;
+                dp[kb2][e2] = 0.f;
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; kb2++) {
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    row_frag<D>(ksm, kb2 * 32, lq, hh, ks), qf[ks], s[kb2], 0, 0, 0);
+                dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    row_frag<D>(vsm, kb2 * 32, lq, hh, ks), dof[ks], dp[kb2], 0, 0, 0);
+            }
+        // dS^T packed as B operands: dsk[kk] for 16-key step kk (key 16kk + 8r + 4hh + t)
+        bf16x8 dsk[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            const int kb2 = kk >> 1, s2 = kk & 1;
+#pragma unroll
+            for (int r = 0; r < 2; r++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int e2 = (2 * s2 + r) * 4 + t;
+                    const int c = kb2 * 32 + 8 * (2 * s2 + r) + t;  // minus 4hh, see L1
+                    const bool vis = (uint32_t)(c - L1) <= n1;
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb2][e2], c2, -lse2)) : 0.f;
+                    dsk[kk][4 * r + t] = (__bf16)(p * (dp[kb2][e2] - Dr));
+                }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+            for (int db = 0; db < DB; db++)
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    tr_frag<D>(ksm, kk, db, tr_row, tr_col), dsk[kk], dqacc[db], 0, 0, 0);
+    };
+    if (e1 > e0) issue(a.col[e0], stage0);
+    for (int e = e0; e < e1; e += 2) {
+        tile(e, stage0, stage1);
+        if (e + 1 < e1) tile(e + 1, stage1, stage0);
+    }
+
+    if (myrow < N) {
+        __bf16 *op = (__bf16 *)a.dq + rowidx * D;
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                bf16x4 w;
+#pragma unroll
+                for (int j = 0; j < 4; j++) w[j] = (__bf16)(dqacc[db][i * 4 + j] * a.scale);
+                *(bf16x4 *)(op + db * 32 + 8 * i + 4 * hh) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
+void dkdv_kernel(BwdArgs a) {
+    constexpr int NW = 2, KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
+    // stage: [Q rows | dO rows | lse[64] | D[64]]
+    __shared__ __attribute__((aligned(1024))) char stage0[2 * TILEB + 512];
+    __shared__ __attribute__((aligned(1024))) char stage1[2 * TILEB + 512];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hh = lane >> 5;
+    const int N = a.N, W = a.W;
+    const int nkt = (N + BN - 1) / BN;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = L % nkt, g = (L / nkt) % a.Hkv, b = L / (nkt * a.Hkv);
+    const int G = a.H / a.Hkv;
+    const int qlen = a.q_len ? a.q_len[b] : N;
+    const int tq = a.tile_q;
+    const int nqt = (N + tq - 1) / tq;
+
+    const int mykey = kt * BN + wave * 32 + lq;
+    const size_t kvh = (size_t)b * a.Hkv + g;
+    const size_t keyidx = kvh * N + mykey;
+    bf16x8 kf[KS], vf[KS];
+    {
+        const __bf16 *kp = (const __bf16 *)a.k + keyidx * D;
+        const __bf16 *vp = (const __bf16 *)a.v + keyidx * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 z = {0, 0, 0, 0};
+            kf[ks] = __builtin_bit_cast(bf16x8, (mykey < N) ? ld16(kp + ks * 16 + hh * 8) : z);
+            vf[ks] = __builtin_bit_cast(bf16x8, (mykey < N) ? ld16(vp + ks * 16 + hh * 8) : z);
+        }
+    }
+    // visible query rows of this lane's key: [ka, kb_]; empty if the key is padding
+    const int ka = mykey, kb_ = min(mykey + W - 1, qlen - 1);
+    const bool kempty = mykey >= qlen || kb_ < ka;
+    const float c2 = a.scale * LOG2E;
+
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            dkacc[db][e] = 0.f;
+            dvacc[db][e] = 0.f;
+        }
+
+    // steps: (query head h, 64-row block s0) over query tiles whose class-grid
+    // entry for this key tile is live, rows kt*64 .. kt*64+63+W-1 at most
+    const int qt_lo = (kt * BN) / tq;
+    const int qt_hi = (int)min((long)nqt - 1, ((long)kt * BN + BN - 2 + W) / tq);
+    const int spt = (tq + BN - 1) / BN;  // 64-row steps per query tile
+    const uint8_t *clsb = a.cls + (size_t)b * nqt * nkt;
+    // step index t over (h, qt, sub); returns the next live step at or after t
+    const int qtn = qt_hi - qt_lo + 1;
+    const int nsteps = G * qtn * spt;
+    auto live_from = [&](int t) -> int {
+        for (; t < nsteps; t++) {
+            const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
+            if (clsb[(size_t)qt * nkt + kt] != 0 && qt * tq + sub * BN < N) break;
+        }
+        return t;
+    };
+    auto step_rows = [&](int t, int &hq, int &s0, bool &part) {
+        const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
+        hq = g * G + t / (spt * qtn);
+        s0 = qt * tq + sub * BN;
+        // a full class counts only in-range pairs: steps or key tiles cut by
+        // the array edge are masked too
+        part = clsb[(size_t)qt * nkt + kt] == 2 || s0 + BN > N || kt * BN + BN > N;
+    };
+    auto issue = [&](int t, char *dst) {
+        int hq, s0;
+        bool part;
+        step_rows(t, hq, s0, part);
+        const size_t rb = ((size_t)b * a.H + hq) * N;
+        stage_rows<D, NW>((const __bf16 *)a.q + rb * D, s0, N, dst, wave, lane);
+        stage_rows<D, NW>((const __bf16 *)a.dout + rb * D, s0, N, dst + TILEB, wave, lane);
+        const int rr = min(s0 + lane, N - 1);
+        const float *src = (wave == 0) ? (a.lse + rb + rr) : (a.dvec + rb + rr);
+        __builtin_amdgcn_global_load_lds((const void *)src, (void *)(dst + 2 * TILEB + wave * 256),
+                                         4, 0, 0);
+    };
+
+    const int tr_j = lane & 15;
+    const int tr_row = 4 * hh + (tr_j >> 2);
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);
+
+    auto step = [&](int t, const char *cur, char *nxt, int tnext) {
+        __syncthreads();
+        if (tnext < nsteps) issue(tnext, nxt);
+        int hq, s0;
+        bool part;
+        step_rows(t, hq, s0, part);
+        (void)hq;
+        const char *qsm = cur;
+        const char *dsm = cur + TILEB;
+        const float *lsm = (const float *)(cur + 2 * TILEB);
+        const float *Dsm = lsm + 64;
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            f32x16 s, dp;
+#pragma unroll
+            for (int e2 = 0; e2 < 16; e2++) {
+                s[e2] = 0.f;
+                dp[e2] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qsm, rb * 32, lq, hh, ks),
+                                                            kf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dsm, rb * 32, lq, hh, ks),
+                                                             vf[ks], dp, 0, 0, 0);
+            }
+            // rows of C element 4i+j: q = s0 + rb*32 + 8i + 4hh + j
+            const int qb = s0 + rb * 32 + 4 * hh;
+            const int L1 = kempty ? -(1 << 20) : ka - qb;
+            const uint32_t n1 = kempty ? 0u : (uint32_t)(kb_ - ka);
+            bf16x8 pk[2], dsk[2];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const f32x4 lse4 = *(const f32x4 *)(lsm + rb * 32 + 8 * i + 4 * hh);
+                const f32x4 D4 = *(const f32x4 *)(Dsm + rb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int c = 8 * i + j;
+                    const bool vis = !part || ((uint32_t)(c - L1) <= n1);
+                    const float p =
+                        vis ? __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], c2, -lse4[j] * LOG2E)) : 0.f;
+                    const float ds = p * (dp[4 * i + j] - D4[j]);
+                    // k index hh*8 + 4r + t of 16-row step kk = q 16kk + 8r + 4hh + t
+                    pk[i >> 1][4 * (i & 1) + j] = (__bf16)p;
+                    dsk[i >> 1][4 * (i & 1) + j] = (__bf16)ds;
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_frag<D>(dsm + rb * 32 * ROWB, kk, db, tr_row, tr_col), pk[kk],
+                        dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_frag<D>(qsm + rb * 32 * ROWB, kk, db, tr_row, tr_col), dsk[kk],
+                        dkacc[db], 0, 0, 0);
+                }
+        }
+    };
+    int t = live_from(0);
+    if (t < nsteps) issue(t, stage0);
+    while (t < nsteps) {
+        const int t1 = live_from(t + 1);
+        step(t, stage0, stage1, t1);
+        if (t1 >= nsteps) break;
+        const int t2 = live_from(t1 + 1);
+        step(t1, stage1, stage0, t2);
+        t = t2;
+    }
+
+    if (mykey < N) {
+        __bf16 *kp = (__bf16 *)a.dk + keyidx * D;
+        __bf16 *vp = (__bf16 *)a.dv + keyidx * D;
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                bf16x4 wk, wv;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    wk[j] = (__bf16)(dkacc[db][i * 4 + j] * a.scale);
+                    wv[j] = (__bf16)dvacc[db][i * 4 + j];
+                }
+                *(bf16x4 *)(kp + db * 32 + 8 * i + 4 * hh) = wk;
+                *(bf16x4 *)(vp + db * 32 + 8 * i + 4 * hh) = wv;
+            }
+    }
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
+    hipError_t e;
+    const int NWq = a.tile_q == 128 ? 4 : 2;
+    const long nqt = (a.N + 32L * NWq - 1) / (32L * NWq);
+    const long nkt = (a.N + BN - 1) / BN;
+    const long gq = nqt * a.H * a.B, gk = nkt * a.Hkv * a.B;
+    if (gq > 0x7fffffffL || gk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (NWq == 4)
+        hipLaunchKernelGGL((dq_kernel<D, 4>), dim3((unsigned)gq), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)gq), dim3(128), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)gk), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_bf16_supported(const BwdArgs &a) {
+    return a.bf16 && (a.d == 64 || a.d == 128) && a.tile_k == BN &&
+           (a.tile_q == 64 || a.tile_q == 128);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
+    return a.d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+}  // namespace swa

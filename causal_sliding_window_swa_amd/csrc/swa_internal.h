@@ -71,6 +71,9 @@ struct BwdArgs {
     int bf16;
 };
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
+// bf16 MFMA kernels (swa_bwd_bf16.hip): d in {64, 128}, tile_k 64, tile_q in {64, 128}.
+bool bwd_bf16_supported(const BwdArgs &a);
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 
 // Ring bookkeeping (swa_ring.hip): write the new rows into their slots, then
 // advance the state; launch_commit does both (after a chunk's attention).
