@@ -208,13 +208,7 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     if (!a.bf16) return launch_t<float>(a, s);
     if (!bwd_bf16_supported(a)) return launch_t<__bf16>(a, s);
-    // row values D on this path, then the MFMA kernels
-    const long rows = (long)a.B * a.H * a.N;
-    if ((rows + 3) / 4 > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dvec_kernel<__bf16>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                       a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the MFMA dq kernel computes the row values D itself
     return launch_bwd_bf16(a, s);
 }
 

@@ -135,14 +135,32 @@ void dq_kernel(BwdArgs a) {
             dof[ks] = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(dp + ks * 16 + hh * 8) : z);
         }
     }
+    // D = <dO, O> of this row: each lane of the pair (l, l^32) holds half of
+    // the row; the dk/dv kernel (launched after this one) reads it back
+    float Dr;
+    {
+        const __bf16 *op = (const __bf16 *)a.o + rowidx * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 z = {0, 0, 0, 0};
+            const bf16x8 of = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(op + ks * 16 + hh * 8) : z);
+#pragma unroll
+            for (int t = 0; t < 8; t++) acc = fmaf((float)of[t], (float)dof[ks][t], acc);
+        }
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
+                                                        false, false);
+        Dr = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        if (myrow < N && hh == 0) a.dvec[rowidx] = Dr;
+        if (!qvalid) Dr = 0.f;
+    }
     const float c2 = a.scale * LOG2E;
     const float lse2 = qvalid ? a.lse[rowidx] * LOG2E : 0.f;
-    const float Dr = qvalid ? a.dvec[rowidx] : 0.f;
 
     const size_t kvh = (size_t)b * a.Hkv + g;
     const __bf16 *kb = (const __bf16 *)a.k + kvh * (size_t)N * D;
     const __bf16 *vb = (const __bf16 *)a.v + kvh * (size_t)N * D;
-    auto issue = [&](int kt, char *dst) {
+    auto issue = [&](int kt, char *dst) __attribute__((always_inline)) {
         stage_rows<D, NW>(kb, kt * BN, N, dst, wave, lane);
         stage_rows<D, NW>(vb, kt * BN, N, dst + TILEB, wave, lane);
     };
@@ -158,7 +176,7 @@ void dq_kernel(BwdArgs a) {
     const int tr_row = 4 * hh + (tr_j >> 2);
     const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);
 
-    auto tile = [&](int e, const char *cur, char *nxt) {
+    auto tile = [&](int e, const char *cur, char *nxt) __attribute__((always_inline)) {
         const int kt = a.col[e];
         __syncthreads();
         if (e + 1 < e1) issue(a.col[e + 1], nxt);
@@ -292,14 +310,14 @@ void dkdv_kernel(BwdArgs a) {
     // step index t over (h, qt, sub); returns the next live step at or after t
     const int qtn = qt_hi - qt_lo + 1;
     const int nsteps = G * qtn * spt;
-    auto live_from = [&](int t) -> int {
+    auto live_from = [&](int t) __attribute__((always_inline)) -> int  {
         for (; t < nsteps; t++) {
             const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
             if (clsb[(size_t)qt * nkt + kt] != 0 && qt * tq + sub * BN < N) break;
         }
         return t;
     };
-    auto step_rows = [&](int t, int &hq, int &s0, bool &part) {
+    auto step_rows = [&](int t, int &hq, int &s0, bool &part) __attribute__((always_inline)) {
         const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
         hq = g * G + t / (spt * qtn);
         s0 = qt * tq + sub * BN;
@@ -307,7 +325,7 @@ void dkdv_kernel(BwdArgs a) {
         // the array edge are masked too
         part = clsb[(size_t)qt * nkt + kt] == 2 || s0 + BN > N || kt * BN + BN > N;
     };
-    auto issue = [&](int t, char *dst) {
+    auto issue = [&](int t, char *dst) __attribute__((always_inline)) {
         int hq, s0;
         bool part;
         step_rows(t, hq, s0, part);
@@ -337,6 +355,7 @@ void dkdv_kernel(BwdArgs a) {
         const float *Dsm = lsm + 64;
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 s, dp;
 #pragma unroll
             for (int e2 = 0; e2 < 16; e2++) {
@@ -349,7 +368,9 @@ void dkdv_kernel(BwdArgs a) {
                                                             kf[ks], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dsm, rb * 32, lq, hh, ks),
                                                              vf[ks], dp, 0, 0, 0);
+                if (ks & 1) __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_sched_barrier(0);
             // rows of C element 4i+j: q = s0 + rb*32 + 8i + 4hh + j
             const int qb = s0 + rb * 32 + 4 * hh;
             const int L1 = kempty ? -(1 << 20) : ka - qb;
@@ -371,6 +392,7 @@ void dkdv_kernel(BwdArgs a) {
                     dsk[i >> 1][4 * (i & 1) + j] = (__bf16)ds;
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < 2; kk++)
 #pragma unroll
@@ -381,6 +403,7 @@ void dkdv_kernel(BwdArgs a) {
                     dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         tr_frag<D>(qsm + rb * 32 * ROWB, kk, db, tr_row, tr_col), dsk[kk],
                         dkacc[db], 0, 0, 0);
+                    if (db & 1) __builtin_amdgcn_sched_barrier(0);
                 }
         }
     };
