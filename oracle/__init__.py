@@ -62,22 +62,22 @@ class Oracle:
         P = ctypes.c_void_p
         i = ctypes.c_int
         d = ctypes.c_double
-        lib.orc_fwd.argtypes = [i, i, i, i, i, i, P, P, P, P, d, P]
-        lib.orc_fwd.restype = None
-        lib.orc_fwd_rows.argtypes = [i, i, i, i, i, i, P, P, P, P, d, i, P, P, P, P]
-        lib.orc_fwd_rows.restype = None
+        lib.orc_fwd_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, d, P]
+        lib.orc_fwd_sink.restype = None
+        lib.orc_fwd_rows_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, d, i, P, P, P, P]
+        lib.orc_fwd_rows_sink.restype = None
         lib.orc_chunk.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, P, d, P]
         lib.orc_chunk.restype = None
-        lib.orc_decode.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, P, d, P]
-        lib.orc_decode.restype = None
-        lib.orc_blockmask.argtypes = [i, i, i, i, i, i, P, P, P, P, i, P, P, P,
-                                      P, P, P, P, P]
-        lib.orc_blockmask.restype = ctypes.c_int64
-        lib.orc_bwd.argtypes = [i, i, i, i, i, i, P, P, P, P, P, d, P, P, P, P]
-        lib.orc_bwd.restype = None
-        lib.orc_bwd_sel.argtypes = [i, i, i, i, i, i, P, P, P, P, P, d, i, P, P, P, P, i, P,
-                                    P, P, P, P]
-        lib.orc_bwd_sel.restype = None
+        lib.orc_decode_sink.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, d, P]
+        lib.orc_decode_sink.restype = None
+        lib.orc_blockmask_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, i, P, P, P,
+                                           P, P, P, P, P]
+        lib.orc_blockmask_sink.restype = ctypes.c_int64
+        lib.orc_bwd_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, d, P, P, P, P]
+        lib.orc_bwd_sink.restype = None
+        lib.orc_bwd_sel_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, d, i, P, P, P, P,
+                                         i, P, P, P, P, P]
+        lib.orc_bwd_sel_sink.restype = None
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -86,18 +86,20 @@ class Oracle:
     def num_threads(self) -> int:
         return self.lib.orc_num_threads()
 
-    def fwd(self, q, k, v, W: int, scale: float, q_len=None) -> np.ndarray:
-        """Full-sequence SWA forward.  q [B,H,N,d], k/v [B,Hkv,N,d] -> o [B,H,N,d]."""
+    def fwd(self, q, k, v, W: int, scale: float, q_len=None, n_sink: int = 0) -> np.ndarray:
+        """Full-sequence SWA forward.  q [B,H,N,d], k/v [B,Hkv,N,d] -> o [B,H,N,d];
+        n_sink > 0 keeps the first n_sink positions visible as attention sinks."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, H, N, dd = q.shape
         Hkv = k.shape[1]
         ql = _i32(q_len)
         o = np.empty_like(q)
-        self.lib.orc_fwd(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(ql),
-                         float(scale), _ptr(o))
+        self.lib.orc_fwd_sink(B, H, Hkv, N, dd, W, n_sink, _ptr(q), _ptr(k), _ptr(v), _ptr(ql),
+                              float(scale), _ptr(o))
         return o
 
-    def fwd_rows(self, q, k, v, W: int, scale: float, rows, q_len=None) -> np.ndarray:
+    def fwd_rows(self, q, k, v, W: int, scale: float, rows, q_len=None,
+                 n_sink: int = 0) -> np.ndarray:
         """Forward for selected rows only.  rows: int array [n,3] of (b, h, i)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, H, N, dd = q.shape
@@ -106,12 +108,12 @@ class Oracle:
         rb, rh, ri = (np.ascontiguousarray(rows[:, c]) for c in range(3))
         ql = _i32(q_len)
         out = np.empty((rows.shape[0], dd), dtype=np.float64)
-        self.lib.orc_fwd_rows(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(ql),
-                              float(scale), rows.shape[0], _ptr(rb), _ptr(rh), _ptr(ri),
-                              _ptr(out))
+        self.lib.orc_fwd_rows_sink(B, H, Hkv, N, dd, W, n_sink, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(ql), float(scale), rows.shape[0], _ptr(rb), _ptr(rh),
+                                   _ptr(ri), _ptr(out))
         return out
 
-    def bwd(self, q, k, v, dout, W: int, scale: float, q_len=None):
+    def bwd(self, q, k, v, dout, W: int, scale: float, q_len=None, n_sink: int = 0):
         """Gradients of the full-sequence forward for output gradient dout.
         Returns (dq [B,H,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d], lse [B,H,N]); lse is
         the natural-log log-sum-exp of each row's allowed scores (-inf if none)."""
@@ -121,11 +123,12 @@ class Oracle:
         ql = _i32(q_len)
         dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
         lse = np.empty((B, H, N), dtype=np.float64)
-        self.lib.orc_bwd(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ql),
-                         float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(lse))
+        self.lib.orc_bwd_sink(B, H, Hkv, N, dd, W, n_sink, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                              _ptr(ql), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(lse))
         return dq, dk, dv, lse
 
-    def bwd_sel(self, q, k, v, dout, W: int, scale: float, qrows, keys, q_len=None):
+    def bwd_sel(self, q, k, v, dout, W: int, scale: float, qrows, keys, q_len=None,
+                n_sink: int = 0):
         """Gradients for selected entries: dq of rows qrows [n,3] (b, h, i) and
         dk, dv of keys keys [m,3] (b, g, j).  Returns (dq [n,d], dk [m,d], dv [m,d])."""
         q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -139,10 +142,10 @@ class Oracle:
         dq = np.empty((qrows.shape[0], dd))
         dk = np.empty((keys.shape[0], dd))
         dv = np.empty((keys.shape[0], dd))
-        self.lib.orc_bwd_sel(B, H, Hkv, N, dd, W, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
-                             _ptr(ql), float(scale), qrows.shape[0], *[_ptr(x) for x in qc],
-                             _ptr(dq), keys.shape[0], *[_ptr(x) for x in kc], _ptr(dk),
-                             _ptr(dv))
+        self.lib.orc_bwd_sel_sink(B, H, Hkv, N, dd, W, n_sink, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(do), _ptr(ql), float(scale), qrows.shape[0],
+                                  *[_ptr(x) for x in qc], _ptr(dq), keys.shape[0],
+                                  *[_ptr(x) for x in kc], _ptr(dk), _ptr(dv))
         return dq, dk, dv
 
     def chunk(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
@@ -160,22 +163,29 @@ class Oracle:
         return o, kc, vc, rs, cl, npos
 
     def decode(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
-               W: int, scale: float):
+               W: int, scale: float, n_sink: int = 0, sink_k=None, sink_v=None):
         """One decode step (append, then attend).  q [B,H,d], k_new/v_new [B,Hkv,d].
-        Returns (o, k_cache', v_cache', ring_start', cache_len', next_pos')."""
+        Returns (o, k_cache', v_cache', ring_start', cache_len', next_pos'); with
+        n_sink > 0 also sink_k', sink_v' ([B,Hkv,n_sink,d] sink caches)."""
         q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
         kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
         rs, cl, npos = (_i32(x).copy() for x in (ring_start, cache_len, next_pos))
         B, H, dd = q.shape
         Hkv = kn.shape[1]
         o = np.empty_like(q)
-        self.lib.orc_decode(B, H, Hkv, dd, W, _ptr(q), _ptr(kn), _ptr(vn), _ptr(kc),
-                            _ptr(vc), _ptr(rs), _ptr(cl), _ptr(npos), float(scale), _ptr(o))
+        sk = sv = None
+        if n_sink > 0:
+            sk, sv = _f64(sink_k).copy(), _f64(sink_v).copy()
+        self.lib.orc_decode_sink(B, H, Hkv, dd, W, n_sink, _ptr(q), _ptr(kn), _ptr(vn), _ptr(kc),
+                                 _ptr(vc), _ptr(sk), _ptr(sv), _ptr(rs), _ptr(cl), _ptr(npos),
+                                 float(scale), _ptr(o))
+        if n_sink > 0:
+            return o, kc, vc, rs, cl, npos, sk, sv
         return o, kc, vc, rs, cl, npos
 
     def blockmask(self, B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=None,
                   q_len=None, k_len=None, W_ring=0, ring_start=None, cache_len=None,
-                  next_pos=None):
+                  next_pos=None, n_sink=0):
         """Brute-force block metadata.  Returns a dict with cls [B,nqt,nkt] uint8,
         row_ptr [B*nqt+1] int32, col [nnz] int32, col_cls [nnz] uint8 and the six
         statistics named in STAT_NAMES."""
@@ -190,7 +200,8 @@ class Oracle:
         stats = np.zeros(6, dtype=np.int64)
         qs, ks, ql, kl, rs, cl, npos = (_i32(x) for x in (
             q_start, k_start, q_len, k_len, ring_start, cache_len, next_pos))
-        nnz = self.lib.orc_blockmask(B, nq, nk_lin, W, tile_q, tile_k, _ptr(qs), _ptr(ks),
+        nnz = self.lib.orc_blockmask_sink(B, nq, nk_lin, W, n_sink, tile_q, tile_k, _ptr(qs),
+                                          _ptr(ks),
                                      _ptr(ql), _ptr(kl), W_ring, _ptr(rs), _ptr(cl),
                                      _ptr(npos), _ptr(cls), _ptr(row_ptr), _ptr(col),
                                      _ptr(col_cls), _ptr(stats))

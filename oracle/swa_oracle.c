@@ -43,12 +43,22 @@ static int allowed(int64_t qpos, int64_t kpos, int64_t W)
     return kpos <= qpos && kpos >= qpos - W + 1;
 }
 
+/* Window plus attention sinks ("Sparse attention taxonomy" §3.2, the
+ * StreamingLLM rule): the first S tokens stay visible to every later query
+ * besides the last W.  READING: sinks are causal (a sink at position p is
+ * seen by queries at p or later) and a key in both sets counts once.  S = 0
+ * is the plain window. */
+static int visible(int64_t qpos, int64_t kpos, int64_t W, int64_t S)
+{
+    return allowed(qpos, kpos, W) || (kpos < S && kpos <= qpos);
+}
+
 /* Attention of one query row over a list of candidate keys given in ascending
  * logical position.  Only keys passing allowed() take part; softmax is
  * normalised over exactly those [M003 §03].  Two passes: the maximum score
  * first, then exp(s - max), so that exp never overflows (the result is the
  * same softmax).  scratch must hold nk doubles. */
-static void attend_row(int d, int64_t W, double scale,
+static void attend_row(int d, int64_t W, int64_t S, double scale,
                        const double *q, int64_t qpos,
                        int nk, const double *const *krow, const double *const *vrow,
                        const int64_t *kpos, double *scratch, double *out)
@@ -62,7 +72,7 @@ static void attend_row(int d, int64_t W, double scale,
     /* s_j = scale * sum_c q_c k_jc for every allowed key */
     for (j = 0; j < nk; j++) {
         double s = 0.0;
-        if (!allowed(qpos, kpos[j], W))
+        if (!visible(qpos, kpos[j], W, S))
             continue;
         for (c = 0; c < d; c++)
             s += q[c] * krow[j][c];
@@ -78,7 +88,7 @@ static void attend_row(int d, int64_t W, double scale,
     /* e_j = exp(s_j - m); l = sum e_j; o = sum e_j v_j / l */
     for (j = 0; j < nk; j++) {
         double e;
-        if (!allowed(qpos, kpos[j], W))
+        if (!visible(qpos, kpos[j], W, S))
             continue;
         e = exp(scratch[j] - m);
         l += e;
@@ -94,9 +104,9 @@ static void attend_row(int d, int64_t W, double scale,
  * i and j.  q_len[b] (NULL = N) is the valid length of sequence b: rows and
  * keys at or past it are padding.  Padded rows are written as 0 (READING).
  * q: [B][H][N][d], k, v: [B][Hkv][N][d], o: [B][H][N][d]. */
-void orc_fwd(int B, int H, int Hkv, int N, int d, int W,
-             const double *q, const double *k, const double *v,
-             const int32_t *q_len, double scale, double *o)
+void orc_fwd_sink(int B, int H, int Hkv, int N, int d, int W, int S,
+                  const double *q, const double *k, const double *v,
+                  const int32_t *q_len, double scale, double *o)
 {
     int64_t b, h;
     const int G = H / Hkv;
@@ -132,16 +142,23 @@ void orc_fwd(int B, int H, int Hkv, int N, int d, int W,
                     vr[j] = vb + (int64_t)j * d;
                     kp[j] = j;
                 }
-                attend_row(d, W, scale, qi, i, len, kr, vr, kp, sc, oi);
+                attend_row(d, W, S, scale, qi, i, len, kr, vr, kp, sc, oi);
                 free(kr); free(vr); free(kp); free(sc);
             }
         }
     }
 }
 
+void orc_fwd(int B, int H, int Hkv, int N, int d, int W,
+             const double *q, const double *k, const double *v,
+             const int32_t *q_len, double scale, double *o)
+{
+    orc_fwd_sink(B, H, Hkv, N, d, W, 0, q, k, v, q_len, scale, o);
+}
+
 /* The same forward, for a list of selected rows only (for large inputs).
  * Row r is (rb[r], rh[r], ri[r]); its output goes to o_rows + r*d. */
-void orc_fwd_rows(int B, int H, int Hkv, int N, int d, int W,
+void orc_fwd_rows_sink(int B, int H, int Hkv, int N, int d, int W, int S,
                   const double *q, const double *k, const double *v,
                   const int32_t *q_len, double scale,
                   int nrows, const int32_t *rb, const int32_t *rh, const int32_t *ri,
@@ -178,9 +195,18 @@ void orc_fwd_rows(int B, int H, int Hkv, int N, int d, int W,
             vr[j] = vb + (int64_t)j * d;
             kp[j] = j;
         }
-        attend_row(d, W, scale, qi, i, len, kr, vr, kp, sc, oi);
+        attend_row(d, W, S, scale, qi, i, len, kr, vr, kp, sc, oi);
         free(kr); free(vr); free(kp); free(sc);
     }
+}
+
+void orc_fwd_rows(int B, int H, int Hkv, int N, int d, int W,
+                  const double *q, const double *k, const double *v,
+                  const int32_t *q_len, double scale,
+                  int nrows, const int32_t *rb, const int32_t *rh, const int32_t *ri,
+                  double *o_rows)
+{
+    orc_fwd_rows_sink(B, H, Hkv, N, d, W, 0, q, k, v, q_len, scale, nrows, rb, rh, ri, o_rows);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -262,7 +288,7 @@ void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
 #pragma omp parallel for schedule(dynamic, 4)
             for (t = 0; t < Tq; t++) {
                 double *sc = malloc(sizeof(*sc) * (size_t)nk);
-                attend_row(d, W, scale,
+                attend_row(d, W, 0, scale,
                            q + (((int64_t)b * H + h) * Tq + t) * d, p0 + t,
                            nk, kr, vr, kp, sc,
                            o + (((int64_t)b * H + h) * Tq + t) * d);
@@ -286,18 +312,32 @@ void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
  * (READING: append, then attend, so the ring holds exactly the W positions
  * the new query may see), then the query at the new token's position attends
  * over the ring's valid slots taken in logical order.
+ * With S > 0 sink tokens ("Sparse attention taxonomy" §3.2: the first tokens
+ * are kept besides the last W) the first S positions also live in a sink
+ * cache sink_k, sink_v [B][Hkv][S][d]: a token appended at position p < S is
+ * copied there as well, and the query also attends over the sink positions
+ * that the ring no longer holds (each position counted once; READING).
  * q: [B][H][d]; k_new, v_new: [B][Hkv][d]; cache and state as orc_chunk. */
-void orc_decode(int B, int H, int Hkv, int d, int W,
-                const double *q, const double *k_new, const double *v_new,
-                double *k_cache, double *v_cache,
-                int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
-                double scale, double *o)
+void orc_decode_sink(int B, int H, int Hkv, int d, int W, int S,
+                     const double *q, const double *k_new, const double *v_new,
+                     double *k_cache, double *v_cache, double *sink_k, double *sink_v,
+                     int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                     double scale, double *o)
 {
     int b;
     const int G = H / Hkv;
     for (b = 0; b < B; b++) {
-        int64_t qpos;
-        int h, len;
+        int64_t qpos, oldest;
+        int h, len, nsink, g;
+        if (S > 0 && next_pos[b] < S) {
+            for (g = 0; g < Hkv; g++) {
+                const int64_t slot = ((int64_t)b * Hkv + g) * S + next_pos[b];
+                memcpy(sink_k + slot * d, k_new + ((int64_t)b * Hkv + g) * d,
+                       sizeof(double) * (size_t)d);
+                memcpy(sink_v + slot * d, v_new + ((int64_t)b * Hkv + g) * d,
+                       sizeof(double) * (size_t)d);
+            }
+        }
         ring_append_one(Hkv, W, d,
                         k_cache + (int64_t)b * Hkv * W * d,
                         v_cache + (int64_t)b * Hkv * W * d,
@@ -306,27 +346,48 @@ void orc_decode(int B, int H, int Hkv, int d, int W,
                         (int64_t)d);
         qpos = (int64_t)next_pos[b] - 1;
         len = cache_len[b];
+        oldest = (int64_t)next_pos[b] - len; /* oldest position still in the ring */
+        nsink = (int)(S < oldest ? S : oldest);
+        if (nsink < 0)
+            nsink = 0;
 #pragma omp parallel for schedule(static)
         for (h = 0; h < H; h++) {
-            const int64_t g = h / G;
-            const double *kc = k_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
-            const double *vc = v_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
-            const double **kr = malloc(sizeof(*kr) * (size_t)len);
-            const double **vr = malloc(sizeof(*vr) * (size_t)len);
-            int64_t *kp = malloc(sizeof(*kp) * (size_t)len);
-            double *sc = malloc(sizeof(*sc) * (size_t)len);
+            const int64_t gg = h / G;
+            const double *kc = k_cache + ((int64_t)b * Hkv + gg) * (int64_t)W * d;
+            const double *vc = v_cache + ((int64_t)b * Hkv + gg) * (int64_t)W * d;
+            const int n = nsink + len;
+            const double **kr = malloc(sizeof(*kr) * (size_t)(n > 0 ? n : 1));
+            const double **vr = malloc(sizeof(*vr) * (size_t)(n > 0 ? n : 1));
+            int64_t *kp = malloc(sizeof(*kp) * (size_t)(n > 0 ? n : 1));
+            double *sc = malloc(sizeof(*sc) * (size_t)(n > 0 ? n : 1));
             int r;
+            /* sink positions the ring has dropped, then the ring in logical order */
+            for (r = 0; r < nsink; r++) {
+                kr[r] = sink_k + (((int64_t)b * Hkv + gg) * S + r) * d;
+                vr[r] = sink_v + (((int64_t)b * Hkv + gg) * S + r) * d;
+                kp[r] = r;
+            }
             for (r = 0; r < len; r++) {
                 const int slot = (ring_start[b] + r) % W;
-                kr[r] = kc + (int64_t)slot * d;
-                vr[r] = vc + (int64_t)slot * d;
-                kp[r] = (int64_t)next_pos[b] - len + r;
+                kr[nsink + r] = kc + (int64_t)slot * d;
+                vr[nsink + r] = vc + (int64_t)slot * d;
+                kp[nsink + r] = (int64_t)next_pos[b] - len + r;
             }
-            attend_row(d, W, scale, q + ((int64_t)b * H + h) * d, qpos,
-                       len, kr, vr, kp, sc, o + ((int64_t)b * H + h) * d);
+            attend_row(d, W, S, scale, q + ((int64_t)b * H + h) * d, qpos,
+                       n, kr, vr, kp, sc, o + ((int64_t)b * H + h) * d);
             free(kr); free(vr); free(kp); free(sc);
         }
     }
+}
+
+void orc_decode(int B, int H, int Hkv, int d, int W,
+                const double *q, const double *k_new, const double *v_new,
+                double *k_cache, double *v_cache,
+                int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                double scale, double *o)
+{
+    orc_decode_sink(B, H, Hkv, d, W, 0, q, k_new, v_new, k_cache, v_cache, NULL, NULL,
+                    ring_start, cache_len, next_pos, scale, o);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -346,13 +407,13 @@ void orc_decode(int B, int H, int Hkv, int d, int W,
  * (row_ptr, col, col_cls); stats[6] = valid pairs, covered coordinates
  * (in-range area of live blocks), distinct keys touched, live, full, partial
  * blocks, each summed over b.  Returns the number of live blocks. */
-int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
-                      const int32_t *q_start, const int32_t *k_start,
-                      const int32_t *q_len, const int32_t *k_len,
-                      int W_ring, const int32_t *ring_start,
-                      const int32_t *cache_len, const int32_t *next_pos,
-                      uint8_t *cls, int32_t *row_ptr, int32_t *col,
-                      uint8_t *col_cls, int64_t *stats)
+int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, int tile_k,
+                           const int32_t *q_start, const int32_t *k_start,
+                           const int32_t *q_len, const int32_t *k_len,
+                           int W_ring, const int32_t *ring_start,
+                           const int32_t *cache_len, const int32_t *next_pos,
+                           uint8_t *cls, int32_t *row_ptr, int32_t *col,
+                           uint8_t *col_cls, int64_t *stats)
 {
     const int nk = W_ring + nk_lin;
     const int nqt = (nq + tile_q - 1) / tile_q;
@@ -403,7 +464,7 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
                 int ii, jj;
                 for (ii = i0; ii < i1; ii++)
                     for (jj = j0; jj < j1; jj++)
-                        if (qok[ii] && kok[jj] && allowed(qpos[ii], kpos[jj], W))
+                        if (qok[ii] && kok[jj] && visible(qpos[ii], kpos[jj], W, S))
                             count++;
                 counts[(int64_t)qt * nkt + kt] = count;
             }
@@ -414,7 +475,7 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
             int ii;
             touched[j] = 0;
             for (ii = 0; ii < nq && kok[j]; ii++)
-                if (qok[ii] && allowed(qpos[ii], kpos[j], W)) {
+                if (qok[ii] && visible(qpos[ii], kpos[j], W, S)) {
                     touched[j] = 1;
                     break;
                 }
@@ -450,6 +511,19 @@ int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
     return nnz;
 }
 
+int64_t orc_blockmask(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
+                      const int32_t *q_start, const int32_t *k_start,
+                      const int32_t *q_len, const int32_t *k_len,
+                      int W_ring, const int32_t *ring_start,
+                      const int32_t *cache_len, const int32_t *next_pos,
+                      uint8_t *cls, int32_t *row_ptr, int32_t *col,
+                      uint8_t *col_cls, int64_t *stats)
+{
+    return orc_blockmask_sink(B, nq, nk_lin, W, 0, tile_q, tile_k, q_start, k_start, q_len,
+                              k_len, W_ring, ring_start, cache_len, next_pos, cls, row_ptr,
+                              col, col_cls, stats);
+}
+
 /* Threads the OpenMP runtime will use (for reporting). */
 int orc_num_threads(void)
 {
@@ -479,7 +553,7 @@ int orc_num_threads(void)
 
 /* Log-sum-exp of row i's allowed scores and D_i = sum_j P_ij <dout_i, v_j>.
  * Returns 0 (and leaves the outputs untouched) when the row sees no key. */
-static int row_stats(int d, int W, int len, double scale, const double *qi, int64_t i,
+static int row_stats(int d, int W, int S, int len, double scale, const double *qi, int64_t i,
                      const double *kb, const double *vb, const double *doi,
                      double *lse, double *D)
 {
@@ -488,7 +562,7 @@ static int row_stats(int d, int W, int len, double scale, const double *qi, int6
     double m = -INFINITY, l = 0.0, dd = 0.0;
     for (j = 0; j < len; j++) {
         double s = 0.0;
-        if (!allowed(i, j, W))
+        if (!visible(i, j, W, S))
             continue;
         for (c = 0; c < d; c++)
             s += qi[c] * kb[j * d + c];
@@ -501,7 +575,7 @@ static int row_stats(int d, int W, int len, double scale, const double *qi, int6
         return 0;
     for (j = 0; j < len; j++) {
         double s = 0.0;
-        if (!allowed(i, j, W))
+        if (!visible(i, j, W, S))
             continue;
         for (c = 0; c < d; c++)
             s += qi[c] * kb[j * d + c];
@@ -510,7 +584,7 @@ static int row_stats(int d, int W, int len, double scale, const double *qi, int6
     *lse = m + log(l);
     for (j = 0; j < len; j++) {
         double s = 0.0, p, dp = 0.0;
-        if (!allowed(i, j, W))
+        if (!visible(i, j, W, S))
             continue;
         for (c = 0; c < d; c++)
             s += qi[c] * kb[j * d + c];
@@ -524,7 +598,7 @@ static int row_stats(int d, int W, int len, double scale, const double *qi, int6
 }
 
 /* dq_i = scale sum_j P_ij (dP_ij - D_i) k_j over row i's allowed keys. */
-static void row_dq(int d, int W, int len, double scale, const double *qi, int64_t i,
+static void row_dq(int d, int W, int S, int len, double scale, const double *qi, int64_t i,
                    const double *kb, const double *vb, const double *doi, double lse,
                    double D, double *dqi)
 {
@@ -534,7 +608,7 @@ static void row_dq(int d, int W, int len, double scale, const double *qi, int64_
         dqi[c] = 0.0;
     for (j = 0; j < len; j++) {
         double s = 0.0, p, dp = 0.0, ds;
-        if (!allowed(i, j, W))
+        if (!visible(i, j, W, S))
             continue;
         for (c = 0; c < d; c++)
             s += qi[c] * kb[j * d + c];
@@ -550,7 +624,7 @@ static void row_dq(int d, int W, int len, double scale, const double *qi, int64_
 /* dk_j, dv_j of key j of kv head g of sequence b: sums over the rows of every
  * query head of the group that see key j.  lse/D: per-row values ([B][H][N]),
  * valid where ok[] is set. */
-static void key_grad(int H, int G, int N, int d, int W, int len, double scale, int64_t b,
+static void key_grad(int H, int G, int N, int d, int W, int S, int len, double scale, int64_t b,
                      int64_t g, int64_t j, const double *q, const double *kb,
                      const double *vb, const double *dout, const double *lse,
                      const double *Dv, const unsigned char *ok, double *dkj, double *dvj)
@@ -569,7 +643,7 @@ static void key_grad(int H, int G, int N, int d, int W, int len, double scale, i
             const double *qi = q + row * d;
             const double *doi = dout + row * d;
             double s = 0.0, p, dp = 0.0, ds;
-            if (!allowed(i, j, W) || !ok[row])
+            if (!visible(i, j, W, S) || !ok[row])
                 continue;
             for (c = 0; c < d; c++)
                 s += qi[c] * kb[j * d + c];
@@ -588,9 +662,9 @@ static void key_grad(int H, int G, int N, int d, int W, int len, double scale, i
 /* Full backward.  q, dout, dq: [B][H][N][d]; k, v, dk, dv: [B][Hkv][N][d];
  * lse_out (may be NULL): [B][H][N] natural-log log-sum-exp of each row's
  * allowed scores, -inf for rows that see no key. */
-void orc_bwd(int B, int H, int Hkv, int N, int d, int W, const double *q, const double *k,
-             const double *v, const double *dout, const int32_t *q_len, double scale,
-             double *dq, double *dk, double *dv, double *lse_out)
+void orc_bwd_sink(int B, int H, int Hkv, int N, int d, int W, int S, const double *q,
+                  const double *k, const double *v, const double *dout, const int32_t *q_len,
+                  double scale, double *dq, double *dk, double *dv, double *lse_out)
 {
     const int G = H / Hkv;
     const int64_t rows = (int64_t)B * H * N;
@@ -607,10 +681,10 @@ void orc_bwd(int B, int H, int Hkv, int N, int d, int W, const double *q, const 
         const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
         const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
         int c;
-        ok[r] = (unsigned char)row_stats(d, W, len, scale, q + r * d, i, kb, vb, dout + r * d,
-                                         &lse[r], &Dv[r]);
+        ok[r] = (unsigned char)row_stats(d, W, S, len, scale, q + r * d, i, kb, vb,
+                                         dout + r * d, &lse[r], &Dv[r]);
         if (ok[r])
-            row_dq(d, W, len, scale, q + r * d, i, kb, vb, dout + r * d, lse[r], Dv[r],
+            row_dq(d, W, S, len, scale, q + r * d, i, kb, vb, dout + r * d, lse[r], Dv[r],
                    dq + r * d);
         else
             for (c = 0; c < d; c++)
@@ -624,20 +698,28 @@ void orc_bwd(int B, int H, int Hkv, int N, int d, int W, const double *q, const 
         const int len = q_len ? q_len[b] : N;
         const double *kb = k + ((b * Hkv + g) * (int64_t)N) * d;
         const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
-        key_grad(H, G, N, d, W, len, scale, b, g, j, q, kb, vb, dout, lse, Dv, ok,
+        key_grad(H, G, N, d, W, S, len, scale, b, g, j, q, kb, vb, dout, lse, Dv, ok,
                  dk + key * d, dv + key * d);
     }
     free(lse); free(Dv); free(ok);
 }
 
+void orc_bwd(int B, int H, int Hkv, int N, int d, int W, const double *q, const double *k,
+             const double *v, const double *dout, const int32_t *q_len, double scale,
+             double *dq, double *dk, double *dv, double *lse_out)
+{
+    orc_bwd_sink(B, H, Hkv, N, d, W, 0, q, k, v, dout, q_len, scale, dq, dk, dv, lse_out);
+}
+
 /* The same gradients for selected entries only (large inputs): dq of rows
  * (qb, qh, qi)[r] and dk, dv of keys (kb_, kg, kj)[r].  Row values are
  * computed for exactly the rows each selection needs. */
-void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
-                 const double *k, const double *v, const double *dout, const int32_t *q_len,
-                 double scale, int nq_sel, const int32_t *qb, const int32_t *qh,
-                 const int32_t *qi, double *dq_rows, int nk_sel, const int32_t *kb_,
-                 const int32_t *kg, const int32_t *kj, double *dk_rows, double *dv_rows)
+void orc_bwd_sel_sink(int B, int H, int Hkv, int N, int d, int W, int S, const double *q,
+                      const double *k, const double *v, const double *dout,
+                      const int32_t *q_len, double scale, int nq_sel, const int32_t *qb,
+                      const int32_t *qh, const int32_t *qi, double *dq_rows, int nk_sel,
+                      const int32_t *kb_, const int32_t *kg, const int32_t *kj,
+                      double *dk_rows, double *dv_rows)
 {
     const int G = H / Hkv;
     int r;
@@ -651,8 +733,8 @@ void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
         const double *vb = v + ((b * Hkv + g) * (int64_t)N) * d;
         double lse, D;
         int c;
-        if (row_stats(d, W, len, scale, q + row * d, i, kb, vb, dout + row * d, &lse, &D))
-            row_dq(d, W, len, scale, q + row * d, i, kb, vb, dout + row * d, lse, D,
+        if (row_stats(d, W, S, len, scale, q + row * d, i, kb, vb, dout + row * d, &lse, &D))
+            row_dq(d, W, S, len, scale, q + row * d, i, kb, vb, dout + row * d, lse, D,
                    dq_rows + (int64_t)r * d);
         else
             for (c = 0; c < d; c++)
@@ -670,19 +752,30 @@ void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
         int64_t h;
         for (h = g * G; h < (g + 1) * G; h++) {
             int64_t i;
-            const int64_t iend = (j + W < N) ? j + W : N;
+            /* rows that can see key j: j .. j+W-1, or every later row for a sink */
+            const int64_t iend = (j < S || j + W >= N) ? N : j + W;
 #pragma omp parallel for schedule(dynamic, 4)
             for (i = j; i < iend; i++) {
                 const int64_t row = (b * H + h) * (int64_t)N + i;
-                ok[h * N + i] = (unsigned char)row_stats(d, W, len, scale, q + row * d, i, kb,
-                                                         vb, dout + row * d, &lse[h * N + i],
-                                                         &Dv[h * N + i]);
+                ok[h * N + i] = (unsigned char)row_stats(d, W, S, len, scale, q + row * d, i,
+                                                         kb, vb, dout + row * d,
+                                                         &lse[h * N + i], &Dv[h * N + i]);
             }
         }
         /* key_grad indexes row values as [b][h][i]; view this sequence's slice */
-        key_grad(H, G, N, d, W, len, scale, 0, g, j, q + b * (int64_t)H * N * d, kb, vb,
+        key_grad(H, G, N, d, W, S, len, scale, 0, g, j, q + b * (int64_t)H * N * d, kb, vb,
                  dout + b * (int64_t)H * N * d, lse, Dv, ok, dk_rows + (int64_t)r * d,
                  dv_rows + (int64_t)r * d);
         free(lse); free(Dv); free(ok);
     }
+}
+
+void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
+                 const double *k, const double *v, const double *dout, const int32_t *q_len,
+                 double scale, int nq_sel, const int32_t *qb, const int32_t *qh,
+                 const int32_t *qi, double *dq_rows, int nk_sel, const int32_t *kb_,
+                 const int32_t *kg, const int32_t *kj, double *dk_rows, double *dv_rows)
+{
+    orc_bwd_sel_sink(B, H, Hkv, N, d, W, 0, q, k, v, dout, q_len, scale, nq_sel, qb, qh, qi,
+                     dq_rows, nk_sel, kb_, kg, kj, dk_rows, dv_rows);
 }

@@ -607,6 +607,119 @@ def pin_bwd_selection_matches(O):
         assert np.array_equal(sk[r], dk[b, g, j]) and np.array_equal(sv[r], dv[b, g, j])
 
 
+# ---------------------------------------------------------------------------
+# Attention sinks ("Sparse attention taxonomy" §3.2: StreamingLLM keeps the
+# first 4 tokens besides the most recent W, a rule on positions only).
+
+def _sink_mask(n, W, S):
+    """Causal band of library triangles plus the causal part of the first S
+    columns."""
+    causal = np.tril(np.ones((n, n), dtype=bool), 0)
+    cols = np.zeros((n, n), dtype=bool)
+    cols[:, :S] = True
+    return _band_mask(n, n, W) | (cols & causal)
+
+
+def pin_sink_visible_sets(O):
+    """The first 4 tokens plus the last W=3, written out from the page's rule:
+    row 10 sees {0,1,2,3,8,9,10}; row 5 sees {0..5} (window 3..5 meets the
+    sinks); row 2 sees {0,1,2}; row 0 sees {0}."""
+    m = O.blockmask(1, 16, 16, 3, 1, 1, n_sink=4)
+    vis = m["cls"][0] > 0
+    want = {10: {0, 1, 2, 3, 8, 9, 10}, 5: {0, 1, 2, 3, 4, 5}, 2: {0, 1, 2}, 0: {0},
+            15: {0, 1, 2, 3, 13, 14, 15}}
+    for r, keys in want.items():
+        assert set(np.nonzero(vis[r])[0].tolist()) == keys, r
+
+
+def pin_sink_pair_counts_and_blocks(O):
+    """Visible pairs = sum over rows of min(t+1, W) + max(0, min(S, t-W+1)); the
+    block metadata with sinks equals a numpy aggregation of the element mask,
+    with lengths and ragged tiles."""
+    for N, W, S in ((40, 5, 4), (33, 1, 2), (64, 70, 4), (50, 8, 12)):
+        m = O.blockmask(1, N, N, W, 16, 8, n_sink=S)
+        want = sum(min(t + 1, W) + max(0, min(S, t - W + 1)) for t in range(N))
+        assert m["valid_pairs"] == want, (N, W, S)
+    N, W, S = 45, 6, 4
+    L = [45, 30]
+    m = O.blockmask(2, N, N, W, 16, 8, q_len=L, k_len=L, n_sink=S)
+    masks = [_sink_mask(N, W, S) & _valid2(N, N, l) for l in L]
+    _check_aggregation(m, masks, 16, 8)
+
+
+def pin_sink_mask_sdpa(O):
+    """Forward with sinks equals SDPA with the library-built mask; n_sink = 0
+    gives the plain window exactly."""
+    rng = _rng(60)
+    B, H, Hkv, N, d = 1, 4, 2, 40, 8
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    for W, S in ((1, 4), (5, 4), (5, 1), (12, 20), (39, 4)):
+        ref = _sdpa(q, k, v, mask=_sink_mask(N, W, S))
+        got = O.fwd(q, k, v, W=W, scale=1.0 / math.sqrt(d), n_sink=S)
+        assert np.max(np.abs(got - ref)) <= 1e-12, (W, S)
+    a = O.fwd(q, k, v, W=5, scale=0.3, n_sink=0)
+    b = O.fwd(q, k, v, W=5, scale=0.3)
+    assert np.array_equal(a, b)
+
+
+def pin_sink_decode_streams_like_full(O):
+    """Streaming every token through decode with sinks (empty ring at the start)
+    gives, at every step, the full-sequence sink forward's row for that
+    position, including steps where the sinks are still inside the window."""
+    rng = _rng(61)
+    B, H, Hkv, T, d, W, S = 2, 4, 2, 23, 6, 5, 3
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    full = O.fwd(q, k, v, W=W, scale=0.5, n_sink=S)
+    kc = np.zeros((B, Hkv, W, d))
+    vc = np.zeros((B, Hkv, W, d))
+    sk = np.zeros((B, Hkv, S, d))
+    sv = np.zeros((B, Hkv, S, d))
+    rs, cl, npos = np.array([0, 2]), np.array([0, 0]), np.array([0, 0])
+    for t in range(T):
+        out = O.decode(q[:, :, t], k[:, :, t], v[:, :, t], kc, vc, rs, cl, npos, W=W,
+                       scale=0.5, n_sink=S, sink_k=sk, sink_v=sv)
+        o, kc, vc, rs, cl, npos, sk, sv = out
+        assert np.max(np.abs(o - full[:, :, t])) <= 1e-12, t
+    assert np.array_equal(sk, k[:, :, :S].transpose(0, 1, 2, 3))
+
+
+def pin_sink_bwd(O):
+    """Gradients with sinks: central differences of the sink forward, and torch
+    autograd through SDPA with the library-built mask."""
+    rng = _rng(62)
+    B, H, Hkv, N, d = 1, 4, 2, 21, 5
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, H, N, d))
+    W, S, sc = 4, 3, 0.7
+    dq, dk, dv, lse = O.bwd(q, k, v, do, W=W, scale=sc, n_sink=S)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = H // Hkv
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1),
+        attn_mask=torch.from_numpy(_sink_mask(N, W, S)), scale=sc)
+    out.backward(torch.from_numpy(do))
+    for got, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        assert np.max(np.abs(got - ref.numpy())) <= 1e-12
+    eps = 1e-5
+    e = rng.standard_normal(k.shape)
+    lp = float((O.fwd(q, k + eps * e, v, W=W, scale=sc, n_sink=S) * do).sum())
+    lm = float((O.fwd(q, k - eps * e, v, W=W, scale=sc, n_sink=S) * do).sum())
+    assert abs((lp - lm) / (2 * eps) - float((dk * e).sum())) <= 1e-6
+    rows = [[0, 1, 20], [0, 3, 2]]
+    keys = [[0, 0, 1], [0, 1, 15], [0, 1, 2]]
+    sq, sk_, sv_ = O.bwd_sel(q, k, v, do, W=W, scale=sc, qrows=rows, keys=keys, n_sink=S)
+    for r, (b, h, i) in enumerate(rows):
+        assert np.array_equal(sq[r], dq[b, h, i])
+    for r, (b, g, j) in enumerate(keys):
+        assert np.array_equal(sk_[r], dk[b, g, j]) and np.array_equal(sv_[r], dv[b, g, j])
+
+
 PINS = [
     pin_window_visible_sets,
     pin_pair_counts,
@@ -629,4 +742,9 @@ PINS = [
     pin_bwd_window_mask_autograd,
     pin_bwd_closed_forms,
     pin_bwd_selection_matches,
+    pin_sink_visible_sets,
+    pin_sink_pair_counts_and_blocks,
+    pin_sink_mask_sdpa,
+    pin_sink_decode_streams_like_full,
+    pin_sink_bwd,
 ]

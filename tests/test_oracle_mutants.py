@@ -29,8 +29,8 @@ MUTANTS = {
     "ring_start_not_advanced": ("*start = (*start + 1) % W;", "*start = *start % W;"),
     "decode_query_position": ("qpos = (int64_t)next_pos[b] - 1;",
                               "qpos = (int64_t)next_pos[b];"),
-    "decode_key_position_shift": ("kp[r] = (int64_t)next_pos[b] - len + r;",
-                                  "kp[r] = (int64_t)next_pos[b] - len + r - 1;"),
+    "decode_key_position_shift": ("kp[nsink + r] = (int64_t)next_pos[b] - len + r;",
+                                  "kp[nsink + r] = (int64_t)next_pos[b] - len + r - 1;"),
     "padding_row_kept": ("if (i >= len) { /* padded row */", "if (i > len) {"),
     "full_threshold": ("(count == area ? 1 : 2)", "(count * 2 >= area ? 1 : 2)"),
     "edge_area_not_clipped": ("const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);",
@@ -46,6 +46,10 @@ MUTANTS = {
     "bwd_lse_no_log": ("*lse = m + log(l);", "*lse = m + l;"),
     "bwd_group_first_head_only": ("for (h = g * G; h < (g + 1) * G; h++) {",
                                   "for (h = g * G; h < g * G + 1; h++) {"),
+    "sink_bound_off_by_one": ("(kpos < S && kpos <= qpos)", "(kpos <= S && kpos <= qpos)"),
+    "sink_not_causal": ("(kpos < S && kpos <= qpos)", "(kpos < S)"),
+    "sink_decode_double_count": ("nsink = (int)(S < oldest ? S : oldest);", "nsink = S;"),
+    "sink_cache_not_written": ("if (S > 0 && next_pos[b] < S) {", "if (S > 0 && next_pos[b] < 0) {"),
     "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
                           "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
 }
