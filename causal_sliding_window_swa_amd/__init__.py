@@ -8,7 +8,7 @@ PyTorch supplies device memory and streams only.  There is no fallback: when
 Functions keep the ABI's names:
 
     swa_blockmask_size(B, nq, nk, tile_q, tile_k)          -> (cls_elems, max_nnz)
-    swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, ...) -> dict (host numpy)
+    swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, ..., n_sink=0) -> dict (host numpy)
     swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None)
     swa_bwd_workspace_size(B, H, N)
     swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, scale=None)
@@ -16,10 +16,11 @@ Functions keep the ABI's names:
                       next_pos, o, W, meta, tile_q, tile_k, scale=None)
     swa_decode_workspace_size(B, H, d, W)
     swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
-               o, workspace, W, scale=None)
+               o, workspace, W, scale=None, n_sink=0, sink_k=None, sink_v=None)
     swa_last_error()
 
-``meta`` is the device copy of a build (``meta_to_device``).  Calls are enqueued
+``meta`` is the device copy of a build (``meta_to_device``); it carries the
+build's tiles and attention-sink count, which swa_fwd and swa_bwd pass on.  Calls are enqueued
 on torch's current stream of the tensors' device.
 """
 from __future__ import annotations
@@ -71,18 +72,18 @@ def lib():
             P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             L.swa_blockmask_size.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                              ctypes.POINTER(ctypes.c_size_t)]
-            L.swa_blockmask_build.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P,
+            L.swa_blockmask_build.argtypes = [I, I, I, I, I, I, I, P, P, P, P, I, P, P, P,
                                               P, P, P, P, ctypes.POINTER(MaskStats)]
-            L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, P]
+            L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, P]
             L.swa_bwd_workspace_size.argtypes = [I, I, I]
             L.swa_bwd_workspace_size.restype = ctypes.c_size_t
-            L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P,
-                                  P, ctypes.c_size_t, F, P]
+            L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
+                                  P, P, ctypes.c_size_t, F, P]
             L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
                                             P, P, P, P, F, P]
             L.swa_decode_workspace_size.argtypes = [I, I, I, I]
             L.swa_decode_workspace_size.restype = ctypes.c_size_t
-            L.swa_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
+            L.swa_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, F, P]
             L.swa_last_error.argtypes = []
             L.swa_last_error.restype = ctypes.c_char_p
@@ -122,7 +123,7 @@ def swa_blockmask_size(B, nq, nk, tile_q, tile_k):
 
 def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=None,
                         q_len=None, k_len=None, W_ring=0, ring_start=None, cache_len=None,
-                        next_pos=None):
+                        next_pos=None, n_sink=0):
     """Host metadata build.  Returns dict: cls [B,nqt,nkt] uint8, row_ptr int32,
     col int32 [nnz], col_cls uint8 [nnz], plus the six statistics."""
     nk = W_ring + nk_lin
@@ -136,13 +137,14 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
     st = MaskStats()
     args = [_np_i32(x) for x in (q_start, k_start, q_len, k_len, ring_start, cache_len,
                                  next_pos)]
-    _check(lib().swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, *[_hp(a) for a in args[:4]],
+    _check(lib().swa_blockmask_build(B, nq, nk_lin, W, n_sink, tile_q, tile_k,
+                                     *[_hp(a) for a in args[:4]],
                                      W_ring, *[_hp(a) for a in args[4:]], _hp(cls),
                                      _hp(row_ptr), _hp(col), _hp(col_cls), ctypes.byref(st)))
     nnz = int(row_ptr[-1])
     out = {"cls": cls[:cls_n].reshape(B, nqt, nkt), "row_ptr": row_ptr,
            "col": col[:nnz].copy(), "col_cls": col_cls[:nnz].copy(),
-           "tile_q": tile_q, "tile_k": tile_k}
+           "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink}
     out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
     return out
 
@@ -157,7 +159,8 @@ def meta_to_device(meta, device):
             "col": torch.from_numpy(col).to(dev),
             "col_cls": torch.from_numpy(ccls).to(dev),
             "cls": torch.from_numpy(np.ascontiguousarray(meta["cls"]).reshape(-1)).to(dev),
-            "tile_q": meta["tile_q"], "tile_k": meta["tile_k"]}
+            "tile_q": meta["tile_q"], "tile_k": meta["tile_k"],
+            "n_sink": meta.get("n_sink", 0)}
 
 
 def _dptr(t):
@@ -196,7 +199,8 @@ def swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None, stream=None):
              tuple(o.shape) == (B, H, N, d), "shape mismatch")
     _require(k.dtype == q.dtype == v.dtype == o.dtype, "dtype mismatch")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    _check(lib().swa_fwd(_dtype_code(q), B, H, Hkv, N, d, W, meta["tile_q"], meta["tile_k"],
+    _check(lib().swa_fwd(_dtype_code(q), B, H, Hkv, N, d, W, meta.get("n_sink", 0),
+                         meta["tile_q"], meta["tile_k"],
                          _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(q_len),
                          _dptr(meta["row_ptr"]), _dptr(meta["col"]), _dptr(meta["col_cls"]),
                          _dptr(lse), ctypes.c_float(scale), _stream(q, stream)))
@@ -224,7 +228,8 @@ def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, s
     _require(len({t.dtype for t in (q, k, v, o, dout, dq, dk, dv)}) == 1, "dtype mismatch")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().swa_bwd(_dtype_code(q), B, H, Hkv, N, d, W, meta["tile_q"], meta["tile_k"],
+    _check(lib().swa_bwd(_dtype_code(q), B, H, Hkv, N, d, W, meta.get("n_sink", 0),
+                         meta["tile_q"], meta["tile_k"],
                          _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(dout), _dptr(lse),
                          _dptr(q_len), _dptr(meta["row_ptr"]), _dptr(meta["col"]),
                          _dptr(meta["cls"]), _dptr(dq), _dptr(dk), _dptr(dv), _dptr(workspace),
@@ -259,8 +264,9 @@ def swa_decode_workspace_size(B, H, d, W) -> int:
 
 
 def swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,
-               workspace, W, scale=None, stream=None):
-    """One decode step; q,o [B,H,d], k_new,v_new [B,Hkv,d], caches [B,Hkv,W,d]."""
+               workspace, W, scale=None, stream=None, n_sink=0, sink_k=None, sink_v=None):
+    """One decode step; q,o [B,H,d], k_new,v_new [B,Hkv,d], caches [B,Hkv,W,d];
+    with n_sink > 0 the sink caches sink_k, sink_v [B,Hkv,n_sink,d] (in/out)."""
     for t in (q, k_new, v_new, k_cache, v_cache, o, ring_start, cache_len, next_pos):
         _require(t.is_contiguous(), "tensors must be contiguous")
     B, H, d = q.shape
@@ -269,7 +275,14 @@ def swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_po
              "cache shape must be [B,Hkv,W,d]")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().swa_decode(_dtype_code(q), B, H, Hkv, d, W, _dptr(q), _dptr(k_new),
+    if n_sink:
+        _require(sink_k is not None and sink_v is not None and
+                 tuple(sink_k.shape) == (B, Hkv, n_sink, d) and
+                 tuple(sink_v.shape) == (B, Hkv, n_sink, d) and sink_k.is_contiguous() and
+                 sink_v.is_contiguous(), "sink caches must be contiguous [B,Hkv,n_sink,d]")
+    _check(lib().swa_decode(_dtype_code(q), B, H, Hkv, d, W, n_sink,
+                            _dptr(sink_k if n_sink else None), _dptr(sink_v if n_sink else None),
+                            _dptr(q), _dptr(k_new),
                             _dptr(v_new), _dptr(k_cache), _dptr(v_cache), _dptr(ring_start),
                             _dptr(cache_len), _dptr(next_pos), _dptr(o), _dptr(workspace),
                             ctypes.c_size_t(ws_bytes), ctypes.c_float(scale),

@@ -25,12 +25,20 @@ struct Run {
     int len;
 };
 
-// Visible keys of a run for a query at logical position t: positions in
-// [t-W+1, t] [M003 §03] intersected with [plo, plo+len-1].
-inline int64_t overlap(int64_t t, int64_t W, const Run &r) {
-    const int64_t lo = std::max(r.plo, t - W + 1);
-    const int64_t hi = std::min(r.plo + r.len - 1, t);
+// Positions of run r inside [lo, hi].
+inline int64_t count_in(const Run &r, int64_t lo, int64_t hi) {
+    lo = std::max(r.plo, lo);
+    hi = std::min(r.plo + r.len - 1, hi);
     return hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Visible keys of a run for a query at logical position t: positions in
+// [t-W+1, t] [M003 §03], plus the sinks [0, min(S-1, t)] ("Sparse attention
+// taxonomy" §3.2), each position counted once.
+inline int64_t overlap(int64_t t, int64_t W, int64_t S, const Run &r) {
+    int64_t n = count_in(r, t - W + 1, t);
+    if (S > 0) n += count_in(r, 0, std::min(S - 1, t)) - count_in(r, t - W + 1, std::min(S - 1, t));
+    return n;
 }
 
 struct KeyAxis {
@@ -84,7 +92,8 @@ extern "C" int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
     return SWA_OK;
 }
 
-extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
+extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q,
+                                   int tile_k,
                                    const int32_t *q_start, const int32_t *k_start,
                                    const int32_t *q_len, const int32_t *k_len, int W_ring,
                                    const int32_t *ring_start, const int32_t *cache_len,
@@ -97,6 +106,10 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q,
                          "tile_q=%d tile_k=%d W_ring=%d)", B, nq, nk_lin, tile_q, tile_k, W_ring);
     if (!cls || !row_ptr || !col || !col_cls)
         return swa::fail(SWA_EINVAL, "blockmask_build: NULL output array");
+    if (n_sink < 0) return swa::fail(SWA_EINVAL, "blockmask_build: n_sink=%d < 0", n_sink);
+    if (n_sink > 0 && W_ring > 0)
+        return swa::fail(SWA_EUNSUPPORTED, "blockmask_build: attention sinks with a ring key "
+                         "axis are not supported");
     if (W_ring > 0) {
         if (W_ring % tile_k != 0)
             return swa::fail(SWA_EINVAL, "blockmask_build: ring size %d not a multiple of "
@@ -149,13 +162,17 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q,
         const int ql = q_len ? q_len[b] : nq;
 
         // distinct keys visible to some valid query: a key at position P is
-        // touched iff some valid query position lies in [P, P+W-1]
+        // touched iff some valid query position lies in [P, P+W-1], or, for a
+        // sink, at or after P
         if (ql > 0) {
             const int nr = ax.runs(0, nk, runs);
+            const int64_t last = qs + ql - 1;
             for (int r = 0; r < nr; r++) {
-                const int64_t lo = std::max(runs[r].plo, qs - W + 1);
-                const int64_t hi = std::min(runs[r].plo + runs[r].len - 1, qs + ql - 1);
-                if (hi >= lo) st.keys_touched += hi - lo + 1;
+                st.keys_touched += count_in(runs[r], qs - W + 1, last);
+                if (n_sink > 0)
+                    st.keys_touched += count_in(runs[r], 0, std::min<int64_t>(n_sink - 1, last)) -
+                                       count_in(runs[r], qs - W + 1,
+                                                std::min<int64_t>(n_sink - 1, last));
             }
         }
         for (int qt = 0; qt < nqt; qt++) {
@@ -174,9 +191,11 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q,
                         pmax = std::max(pmax, runs[r].plo + runs[r].len - 1);
                     }
                     const int64_t tmin = qs + i0, tmax = qs + iv1 - 1;
-                    if (nr > 0 && pmax >= tmin - W + 1 && pmin <= tmax) {
+                    const bool near = pmax >= tmin - W + 1 || pmin < n_sink;
+                    if (nr > 0 && near && pmin <= tmax) {
                         for (int i = i0; i < iv1; i++)
-                            for (int r = 0; r < nr; r++) count += overlap(qs + i, W, runs[r]);
+                            for (int r = 0; r < nr; r++)
+                                count += overlap(qs + i, W, n_sink, runs[r]);
                     }
                 }
                 const uint8_t c = count == 0 ? SWA_BLOCK_SKIP

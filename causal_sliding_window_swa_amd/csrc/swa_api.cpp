@@ -81,8 +81,8 @@ int launched(const char *fn, hipError_t e) {
 
 extern "C" const char *swa_last_error(void) { return swa::g_err; }
 
-extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q,
-                       int tile_k, const void *q, const void *k, const void *v, void *o,
+extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink,
+                       int tile_q, int tile_k, const void *q, const void *k, const void *v, void *o,
                        const int32_t *q_len_dev, const int32_t *row_ptr_dev,
                        const int32_t *col_dev, const uint8_t *col_cls_dev, float *lse_dev,
                        float scale, void *stream) {
@@ -90,6 +90,7 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     swa::clear_error();
     int rc;
     if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
     if (N < 1) return fail(SWA_EINVAL, "%s: N=%d must be >= 1", fn, N);
     if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
@@ -109,6 +110,7 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     a.q_len = q_len_dev;
     a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
     a.lse = lse_dev;
+    a.n_sink = n_sink;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
@@ -119,8 +121,8 @@ extern "C" size_t swa_bwd_workspace_size(int B, int H, int N) {
     return (size_t)B * H * N * sizeof(float);
 }
 
-extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q,
-                       int tile_k, const void *q, const void *k, const void *v, const void *o,
+extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink,
+                       int tile_q, int tile_k, const void *q, const void *k, const void *v, const void *o,
                        const void *dout, const float *lse_dev, const int32_t *q_len_dev,
                        const int32_t *row_ptr_dev, const int32_t *col_dev,
                        const uint8_t *cls_dev, void *dq, void *dk, void *dv, void *workspace,
@@ -129,6 +131,7 @@ extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     swa::clear_error();
     int rc;
     if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
     if (N < 1) return fail(SWA_EINVAL, "%s: N=%d must be >= 1", fn, N);
     if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
@@ -154,6 +157,7 @@ extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     a.row_ptr = row_ptr_dev; a.col = col_dev; a.cls = cls_dev;
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.dvec = (float *)workspace;
+    a.n_sink = n_sink;
     a.scale = scale;
     a.bf16 = dt == SWA_BF16;
     return launched(fn, swa::launch_bwd(a, (hipStream_t)stream));
@@ -210,7 +214,8 @@ extern "C" size_t swa_decode_workspace_size(int B, int H, int d, int W) {
     return (size_t)B * H * swa::decode_max_splits(W) * (size_t)(d + 2) * sizeof(float);
 }
 
-extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, const void *q,
+extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
+                          void *sink_k, void *sink_v, const void *q,
                           const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                           int32_t *ring_start_dev, int32_t *cache_len_dev,
                           int32_t *next_pos_dev, void *o, void *workspace, size_t ws_bytes,
@@ -230,7 +235,16 @@ extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, con
         return fail(SWA_EINVAL, "%s: the ring state arrays are required", fn);
     if (!(scale > 0.f) || scale == INFINITY)
         return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
+    if (n_sink > 0) {
+        const void *sp[] = {sink_k, sink_v};
+        const char *sn[] = {"sink_k", "sink_v"};
+        if ((rc = check_ptrs(fn, sp, sn, 2))) return rc;
+    }
     swa::DecodeArgs a = {};
+    a.n_sink = n_sink;
+    a.sk = sink_k;
+    a.sv = sink_v;
     a.B = B; a.H = H; a.Hkv = Hkv; a.d = d; a.W = W;
     a.q = q; a.k_new = k_new; a.v_new = v_new; a.kc = k_cache; a.vc = v_cache;
     a.ring_start = ring_start_dev; a.cache_len = cache_len_dev; a.next_pos = next_pos_dev;

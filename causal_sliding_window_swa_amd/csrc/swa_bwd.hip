@@ -90,9 +90,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         const int e0 = a.row_ptr[b * nqt + qt], e1 = a.row_ptr[b * nqt + qt + 1];
         for (int e = e0; e < e1; e++) {
             const int kt = a.col[e];
-            const int j0 = max(max(kt * a.tile_k, i - W + 1), 0);
+            // window keys, plus the attention sinks below n_sink
+            const int j0 = max(kt * a.tile_k, (kt * a.tile_k < a.n_sink) ? 0 : i - W + 1);
             const int j1 = min(min((kt + 1) * a.tile_k - 1, i), qlen - 1);
             for (int j = j0; j <= j1; j++) {
+                if (j < i - W + 1 && j >= a.n_sink) continue;
                 float s = 0.f, dp = 0.f, kv[2] = {0.f, 0.f};
 #pragma unroll
                 for (int u = 0; u < 2; u++)
@@ -145,14 +147,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         const int nqt = (N + a.tile_q - 1) / a.tile_q;
         const int nkt = (N + a.tile_k - 1) / a.tile_k;
         const int kt = j / a.tile_k;
-        // query tiles that can reach this key tile: rows kt*tk .. kt*tk+tk-1+W-1
+        // query tiles that can reach this key tile: rows kt*tk .. kt*tk+tk-1+W-1,
+        // or every later row for a tile holding attention sinks
         const int qt0 = (kt * a.tile_k) / a.tile_q;
         const long last = (long)kt * a.tile_k + a.tile_k - 2 + W;
-        const int qt1 = (int)min((long)nqt - 1, last / a.tile_q);
+        const int qt1 = (kt * a.tile_k < a.n_sink) ? nqt - 1
+                                                   : (int)min((long)nqt - 1, last / a.tile_q);
         for (int qt = qt0; qt <= qt1; qt++) {
             if (a.cls[((size_t)b * nqt + qt) * nkt + kt] == 0) continue;
             const int i0 = max(qt * a.tile_q, j);
-            const int i1 = min(min((qt + 1) * a.tile_q - 1, j + W - 1), qlen - 1);
+            const int i1 = min(min((qt + 1) * a.tile_q - 1, (j < a.n_sink) ? qlen - 1 : j + W - 1),
+                               qlen - 1);
             for (int h = g * G; h < (g + 1) * G; h++) {
                 const size_t rbase = ((size_t)b * a.H + h) * N;
                 for (int i = i0; i <= i1; i++) {

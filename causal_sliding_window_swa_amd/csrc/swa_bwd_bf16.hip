@@ -191,6 +191,14 @@ void dq_kernel(BwdArgs a) {
         const bool empty = b1 < a1;
         const int L1 = empty ? -(1 << 20) : a1 - 4 * hh;
         const uint32_t n1 = empty ? 0u : (uint32_t)(b1 - a1);
+        // attention sinks: keys 0 .. n_sink-1 (a second interval)
+        int a2 = -base, b2 = min(a.n_sink - 1, min(myrow, qlen - 1)) - base;
+        if (!qvalid || a.n_sink <= base) b2 = -1;
+        a2 = max(a2, 0);
+        b2 = min(b2, BN - 1);
+        const bool empty2 = b2 < a2;
+        const int L2 = empty2 ? -(1 << 20) : a2 - 4 * hh;
+        const uint32_t n2 = empty2 ? 0u : (uint32_t)(b2 - a2);
 
         f32x16 s[2], dp[2];
 #pragma unroll
@@ -220,7 +228,7 @@ void dq_kernel(BwdArgs a) {
                 for (int t = 0; t < 4; t++) {
                     const int e2 = (2 * s2 + r) * 4 + t;
                     const int c = kb2 * 32 + 8 * (2 * s2 + r) + t;  // minus 4hh, see L1
-                    const bool vis = (uint32_t)(c - L1) <= n1;
+                    const bool vis = ((uint32_t)(c - L1) <= n1) | ((uint32_t)(c - L2) <= n2);
                     const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb2][e2], c2, -lse2)) : 0.f;
                     dsk[kk][4 * r + t] = (__bf16)(p * (dp[kb2][e2] - Dr));
                 }
@@ -287,8 +295,9 @@ void dkdv_kernel(BwdArgs a) {
             vf[ks] = __builtin_bit_cast(bf16x8, (mykey < N) ? ld16(vp + ks * 16 + hh * 8) : z);
         }
     }
-    // visible query rows of this lane's key: [ka, kb_]; empty if the key is padding
-    const int ka = mykey, kb_ = min(mykey + W - 1, qlen - 1);
+    // visible query rows of this lane's key: [ka, kb_] (every later row for an
+    // attention sink); empty if the key is padding
+    const int ka = mykey, kb_ = (mykey < a.n_sink) ? qlen - 1 : min(mykey + W - 1, qlen - 1);
     const bool kempty = mykey >= qlen || kb_ < ka;
     const float c2 = a.scale * LOG2E;
 
@@ -304,7 +313,8 @@ void dkdv_kernel(BwdArgs a) {
     // steps: (query head h, 64-row block s0) over query tiles whose class-grid
     // entry for this key tile is live, rows kt*64 .. kt*64+63+W-1 at most
     const int qt_lo = (kt * BN) / tq;
-    const int qt_hi = (int)min((long)nqt - 1, ((long)kt * BN + BN - 2 + W) / tq);
+    const int qt_hi = (kt * BN < a.n_sink) ? nqt - 1
+                                           : (int)min((long)nqt - 1, ((long)kt * BN + BN - 2 + W) / tq);
     const int spt = (tq + BN - 1) / BN;  // 64-row steps per query tile
     const uint8_t *clsb = a.cls + (size_t)b * nqt * nkt;
     // step index t over (h, qt, sub); returns the next live step at or after t

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
             L += f * wl[w][hq];
             O += f * wo[w][hq][dd];
         }
-        if (nsp == 1) {
+        if (nsp == 1 && a.n_sink == 0) {
             ((__bf16 *)a.o)[((size_t)b * a.H + g * G + hq) * D + dd] =
                 (__bf16)((L > 0.f) ? O / L : 0.f);
             continue;
@@ -316,14 +316,55 @@ __global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// Sum over the D threads of a block (D = 64 or 128).
+template <int D>
+__device__ __forceinline__ float block_sum(float x, float *red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    if (D == 64) return x;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    const float r = red[0] + red[1];
+    __syncthreads();
+    return r;
+}
+
 // grid (B*H), D threads: log-sum-exp merge of the NSP ranges, O = sum / l as
 // bf16; block (b, head 0) then advances the ring state of request b by one
 // token.  NSP is a compile-time constant so every (max, sum) pair (uniform
 // across the block, hence scalar loads) and partial row is loaded before any
-// is used.
-template <int D, int NSP>
+// is used.  SINK: the attention sinks ("Sparse attention taxonomy" §3.2) the
+// ring no longer holds join the merge as one more partial, a token appended
+// at a sink position is copied to the sink cache, and the ring state is left
+// to decode_state_kernel (every block reads it here).
+template <int D, int NSP, bool SINK>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+    float msk = -INFINITY, lsk = 0.f, osk = 0.f;  // sink partial (log2 units)
+    if (SINK) {
+        __shared__ float red[2];
+        const int W = a.W, cl = a.cache_len[b], np = a.next_pos[b];
+        const int cl2 = (cl == W) ? W : cl + 1;
+        const int nsink = min(a.n_sink, np + 1 - cl2);
+        const int G = a.H / a.Hkv, g = h / G, c = threadIdx.x;
+        const float qc = (float)((const __bf16 *)a.q)[(size_t)bh * D + c];
+        const float c2 = a.scale * 1.4426950408889634f;
+        const size_t sbase = ((size_t)b * a.Hkv + g) * a.n_sink;
+        for (int p = 0; p < nsink; p++) {
+            const float kc = (float)((const __bf16 *)a.sk)[(sbase + p) * D + c];
+            const float vc = (float)((const __bf16 *)a.sv)[(sbase + p) * D + c];
+            const float s2 = block_sum<D>(qc * kc, red) * c2;
+            const float mn = fmaxf(msk, s2);
+            const float f = __builtin_amdgcn_exp2f(msk - mn), e = __builtin_amdgcn_exp2f(s2 - mn);
+            lsk = lsk * f + e;
+            osk = osk * f + e * vc;
+            msk = mn;
+        }
+        if (np < a.n_sink && h % G == 0) {  // slot np is not read in this step
+            ((__bf16 *)a.sk)[(sbase + np) * D + c] = ((const __bf16 *)a.k_new)[((size_t)b * a.Hkv + g) * D + c];
+            ((__bf16 *)a.sv)[(sbase + np) * D + c] = ((const __bf16 *)a.v_new)[((size_t)b * a.Hkv + g) * D + c];
+        }
+    }
     const float *ml = a.ws + (size_t)a.B * a.H * NSP * D + (size_t)bh * NSP * 2;
     const float *op = a.ws + (size_t)bh * NSP * D + threadIdx.x;
     float m[NSP], l[NSP], o[NSP];
@@ -333,7 +374,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
         l[s] = ml[2 * s + 1];
         o[s] = op[(size_t)s * D];
     }
-    float M = -INFINITY;
+    float M = msk;
 #pragma unroll
     for (int s = 0; s < NSP; s++) M = fmaxf(M, m[s]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
@@ -344,8 +385,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
         L += f * l[s];
         O += f * o[s];
     }
+    if (SINK) {
+        const float f = __builtin_amdgcn_exp2f(msk - Mu);
+        L += f * lsk;
+        O += f * osk;
+    }
     ((__bf16 *)a.o)[(size_t)bh * D + threadIdx.x] = (__bf16)((L > 0.f) ? O / L : 0.f);
-    if (h == 0 && threadIdx.x == 0) {
+    if (!SINK && h == 0 && threadIdx.x == 0) {
         const int W = a.W, rs = a.ring_start[b], cl = a.cache_len[b];
         const bool full = cl == W;
         a.ring_start[b] = full ? (rs + 1) % W : rs;
@@ -369,29 +415,39 @@ __global__ void decode_state_kernel(int32_t *ring_start, int32_t *cache_len, int
 
 // One range per (request, KV head): the waves merge in LDS and write O, then
 // the ring state advances.  Several ranges: the log-sum-exp combine follows.
+template <int D, bool SINK>
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(a.B * a.H), blk(D);
+    switch (a.n_split) {
+        case 1: hipLaunchKernelGGL((decode_combine_kernel<D, 1, SINK>), grid, blk, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_combine_kernel<D, 2, SINK>), grid, blk, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_combine_kernel<D, 4, SINK>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_combine_kernel<D, 8, SINK>), grid, blk, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_combine_kernel<D, 16, SINK>), grid, blk, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_combine_kernel<D, 32, SINK>), grid, blk, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// One range per (request, KV head) and no sinks: the waves merge in LDS and
+// write O, then the ring state advances.  Otherwise each range writes its
+// partial and the log-sum-exp combine follows (with sinks, then the state).
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs &a, hipStream_t s) {
     hipError_t e;
-    if (a.n_split == 1) {
-        hipLaunchKernelGGL((decode_split_kernel<D, G, 4>), dim3(1, a.Hkv, a.B), dim3(256), 0, s,
-                           a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_split_kernel<D, G, 4>), dim3(a.n_split, a.Hkv, a.B), dim3(256), 0,
+                       s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.n_split == 1 && a.n_sink == 0) {
         hipLaunchKernelGGL(decode_state_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s,
                            a.ring_start, a.cache_len, a.next_pos, a.B, a.W);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_split_kernel<D, G, 4>), dim3(a.n_split, a.Hkv, a.B), dim3(256), 0,
-                       s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 grid(a.B * a.H), blk(D);
-    switch (a.n_split) {
-        case 2: hipLaunchKernelGGL((decode_combine_kernel<D, 2>), grid, blk, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_combine_kernel<D, 4>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_combine_kernel<D, 8>), grid, blk, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((decode_combine_kernel<D, 16>), grid, blk, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((decode_combine_kernel<D, 32>), grid, blk, 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (a.n_sink == 0) return launch_combine<D, false>(a, s);
+    if ((e = launch_combine<D, true>(a, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_state_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a.ring_start,
+                       a.cache_len, a.next_pos, a.B, a.W);
     return hipGetLastError();
 }
 

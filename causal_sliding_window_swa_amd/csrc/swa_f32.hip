@@ -99,7 +99,8 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
                         kr = klin + (size_t)t * d;
                         vr = vlin + (size_t)t * d;
                     }
-                    if (ok && pos <= qpos && pos >= qpos - W + 1) st.add(kr, vr, d, a.scale);
+                    if (ok && pos <= qpos && (pos >= qpos - W + 1 || pos < a.n_sink))
+                        st.add(kr, vr, d, a.scale);
                 }
             }
         }
@@ -134,6 +135,27 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
         const int pos = np + 1 - cl2 + r;
         if (r < cl2 && pos <= qpos && pos >= qpos - W + 1)
             st.add(kring + (size_t)s * d, vring + (size_t)s * d, d, a.scale);
+    }
+    // attention sinks ("Sparse attention taxonomy" §3.2): positions below
+    // n_sink that the ring no longer holds come from the sink cache; a token
+    // appended at a sink position is copied there (that slot is not read in
+    // this step, since the ring still holds it)
+    if (a.n_sink > 0) {
+        const int nsink = min(a.n_sink, np + 1 - cl2);
+        const float *ks = (const float *)a.sk + ((size_t)b * a.Hkv + g) * a.n_sink * d;
+        const float *vs = (const float *)a.sv + ((size_t)b * a.Hkv + g) * a.n_sink * d;
+        for (int p = threadIdx.x; p < nsink; p += 64)
+            st.add(ks + (size_t)p * d, vs + (size_t)p * d, d, a.scale);
+        if (np < a.n_sink && h % (a.H / a.Hkv) == 0) {
+            const float *kn = (const float *)a.k_new + ((size_t)b * a.Hkv + g) * d;
+            const float *vn = (const float *)a.v_new + ((size_t)b * a.Hkv + g) * d;
+            float *kd = (float *)a.sk + (((size_t)b * a.Hkv + g) * a.n_sink + np) * d;
+            float *vd = (float *)a.sv + (((size_t)b * a.Hkv + g) * a.n_sink + np) * d;
+            for (int c = threadIdx.x; c < d; c += 64) {
+                kd[c] = kn[c];
+                vd[c] = vn[c];
+            }
+        }
     }
     const int t = threadIdx.x;
     sm[t] = st.m;

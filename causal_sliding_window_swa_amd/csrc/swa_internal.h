@@ -27,6 +27,7 @@ struct AttnArgs {
     const int32_t *row_ptr, *col;
     const uint8_t *col_cls;
     float *lse;  // mode 0, may be null: [B][H][nq] natural-log row log-sum-exp
+    int n_sink;  // mode 0: keys at positions < n_sink stay visible (attention sinks)
     float scale;
 };
 
@@ -38,6 +39,8 @@ struct DecodeArgs {
     void *o;
     float *ws;
     int n_split;
+    int n_sink;     // attention sinks: sink caches [B][Hkv][n_sink][d] (sk, sv)
+    void *sk, *sv;
     float scale;
 };
 
@@ -67,6 +70,7 @@ struct BwdArgs {
     const uint8_t *cls;  // [B][nqt][nkt] class grid
     void *dq, *dk, *dv;
     float *dvec;  // workspace: [B][H][N] fp32 row values D = <dout, o>
+    int n_sink;
     float scale;
     int bf16;
 };

@@ -235,6 +235,11 @@ void tile_kernel(AttnArgs a) {
                 const int base = kt * BN;       // position of tile key 0
                 a1 = lo_pos - base;
                 b1 = min(qpos, qlen - 1) - base;
+                if (a.n_sink > base) {  // attention sinks: keys 0 .. n_sink-1
+                    two = true;
+                    a2 = -base;
+                    b2 = min(a.n_sink - 1, min(qpos, qlen - 1)) - base;
+                }
             } else if (kt < kp.nrt) {
                 const int off = kp.np - kp.cl;  // position of ring offset r = 0
                 const int rlo = max(0, lo_pos - off), rhi = min(kp.cl - 1, qpos - off);

@@ -86,8 +86,13 @@ int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
  * NULL q_start/k_start mean 0, NULL q_len/k_len mean "all valid"; the ring
  * arrays are ignored when W_ring == 0 and required otherwise.
  *
+ * n_sink >= 0 attention sinks [Taxonomy §3.2, the StreamingLLM rule]: keys
+ * at logical positions below n_sink stay visible to every query at or after
+ * them, besides the window (a key in both counts once); 0 is the plain
+ * window.  Sinks need W_ring == 0 (SWA_EUNSUPPORTED otherwise).
+ *
  * For swa_fwd: q_start = k_start = NULL, nq = nk_lin = N, q_len = k_len =
- *   the per-sequence valid lengths (or NULL), W_ring = 0.
+ *   the per-sequence valid lengths (or NULL), W_ring = 0, the call's n_sink.
  * For swa_prefill_chunk: nq = nk_lin = Tq, q_start = k_start = next_pos,
  *   k_len = NULL, W_ring = W and the ring state the call will see.
  *
@@ -98,7 +103,7 @@ int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
  * positive"], bad sizes, W_ring % tile_k != 0, ring state out of range
  * (ring_start not in [0, W_ring), cache_len not in [0, W_ring],
  * next_pos < cache_len), a negative length, or positions that overflow int32. */
-int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k,
+int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q, int tile_k,
                         const int32_t *q_start, const int32_t *k_start,
                         const int32_t *q_len, const int32_t *k_len,
                         int W_ring, const int32_t *ring_start, const int32_t *cache_len,
@@ -110,8 +115,9 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k
  * q, o [B][H][N][d]; k, v [B][Hkv][N][d]; query row i and key row j sit at
  * logical positions i and j.  q_len_dev: device int32 [B] valid lengths or
  * NULL (= N); rows at or past the length are written as 0.
+ * n_sink: attention sinks as in swa_blockmask_build (0: plain window).
  * row_ptr_dev / col_dev / col_cls_dev: device copies of a swa_blockmask_build
- * with the same B, N, W, tile_q, tile_k and lengths; only listed key tiles
+ * with the same B, N, W, n_sink, tile_q, tile_k and lengths; only listed key tiles
  * are read, and only partial ones are masked per element.  The kernel does
  * not re-check the metadata: metadata of other shapes is a caller error.
  * Supported: SWA_BF16 with d in {64, 128}, (tile_q, tile_k) = (128, 64) or
@@ -122,7 +128,8 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int tile_q, int tile_k
  * which swa_bwd needs.
  * Errors: SWA_EINVAL (W < 1, H % Hkv != 0, N < 1, NULL or misaligned
  * pointers), SWA_EUNSUPPORTED, SWA_EHIP. */
-int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q, int tile_k,
+int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink,
+            int tile_q, int tile_k,
             const void *q, const void *k, const void *v, void *o,
             const int32_t *q_len_dev,
             const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *col_cls_dev,
@@ -140,7 +147,7 @@ size_t swa_bwd_workspace_size(int B, int H, int N);
  *   dv_j = sum_i P_ij dout_i  (visible pairs only; grouped heads summed).
  * q, o, dout, dq [B][H][N][d]; k, v, dk, dv [B][Hkv][N][d], all of dtype dt
  * (fp32 arithmetic inside); lse_dev: the fp32 [B][H][N] that swa_fwd wrote
- * for this q, k, v; q_len_dev as for swa_fwd.  row_ptr_dev / col_dev: the
+ * for this q, k, v and n_sink; q_len_dev as for swa_fwd.  row_ptr_dev / col_dev: the
  * block metadata of swa_fwd (query rows visit their tile's key tiles);
  * cls_dev: its class grid [B][nqt][nkt] (keys visit the query tiles whose
  * entry for their key tile is live).  Padded rows and keys get 0.  The
@@ -149,7 +156,8 @@ size_t swa_bwd_workspace_size(int B, int H, int N);
  * Supported: as swa_fwd for d; any positive tiles matching the metadata.
  * Errors: SWA_EINVAL (as swa_fwd, small workspace), SWA_EUNSUPPORTED,
  * SWA_EHIP. */
-int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int tile_q, int tile_k,
+int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink,
+            int tile_q, int tile_k,
             const void *q, const void *k, const void *v, const void *o, const void *dout,
             const float *lse_dev, const int32_t *q_len_dev,
             const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *cls_dev,
@@ -192,10 +200,17 @@ size_t swa_decode_workspace_size(int B, int H, int d, int W);
  * next_pos (the old value) attends over the ring's valid slots; next_pos
  * grows by one.  workspace: device memory of swa_decode_workspace_size bytes
  * (ws_bytes), no initialisation needed.
+ * n_sink > 0 [Taxonomy §3.2]: sink_k, sink_v [B][Hkv][n_sink][d] (in/out,
+ * dtype dt) hold the rows of logical positions 0 .. n_sink-1; a token
+ * appended at position p < n_sink is also copied to sink slot p, and the
+ * query also attends over the sink positions the ring no longer holds
+ * (below next_pos + 1 - cache_len after the append).  n_sink == 0: the sink
+ * pointers are ignored.
  * Supported: SWA_BF16 with d in {64, 128}, H / Hkv in {1, 2, 4, 8}; SWA_F32 with d a
  * multiple of 4 in [4, 128].
  * Errors: as swa_fwd, plus SWA_EINVAL when ws_bytes is too small. */
-int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W,
+int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
+               void *sink_k, void *sink_v,
                const void *q, const void *k_new, const void *v_new,
                void *k_cache, void *v_cache,
                int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,

@@ -45,14 +45,19 @@ def test_blockmask_rejects_bad_arguments():
         swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, q_len=[9], k_len=[9])
     with pytest.raises(swa.SwaError):  # positions overflowing int32
         swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, q_start=[2**31 - 5], k_start=[0])
+    with pytest.raises(swa.SwaError):  # negative sink count
+        swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, n_sink=-1)
+    with pytest.raises(swa.SwaError):  # sinks with a ring key axis
+        swa.swa_blockmask_build(1, 4, 4, 8, 4, 4, q_start=[8], k_start=[8], W_ring=8,
+                                ring_start=[0], cache_len=[8], next_pos=[8], n_sink=2)
 
 
 P = ctypes.c_void_p
 
 
-def _fwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, tq=128, tk=64, ptr=16):
+def _fwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, tq=128, tk=64, ptr=16, sink=0):
     p = ctypes.c_void_p(ptr)
-    return swa.lib().swa_fwd(dt, B, H, Hkv, N, d, W, tq, tk, p, p, p, p, None, p, p, p,
+    return swa.lib().swa_fwd(dt, B, H, Hkv, N, d, W, sink, tq, tk, p, p, p, p, None, p, p, p,
                              None, ctypes.c_float(0.1), None)
 
 
@@ -67,6 +72,7 @@ def test_fwd_validation_codes():
     assert _fwd(ptr=0) == swa.SWA_EINVAL
     assert _fwd(ptr=8) == swa.SWA_EINVAL  # misaligned
     assert _fwd(dt=7) == swa.SWA_EINVAL
+    assert _fwd(sink=-1) == swa.SWA_EINVAL
     assert "window" in swa.swa_last_error() or True
 
 
@@ -74,7 +80,7 @@ def _bwd(dt=0, B=1, H=4, Hkv=2, N=128, d=128, W=16, ptr=16, ws=None, cls=True):
     p = ctypes.c_void_p(ptr)
     need = swa.swa_bwd_workspace_size(B, H, N)
     wsb = need if ws is None else ws
-    return swa.lib().swa_bwd(dt, B, H, Hkv, N, d, W, 128, 64, p, p, p, p, p, p, None, p, p,
+    return swa.lib().swa_bwd(dt, B, H, Hkv, N, d, W, 0, 128, 64, p, p, p, p, p, p, None, p, p,
                              p if cls else None, p, p, p, p, ctypes.c_size_t(wsb),
                              ctypes.c_float(0.1), None)
 
@@ -109,9 +115,10 @@ def test_chunk_validation_codes():
     assert _chunk(d=80) == swa.SWA_EUNSUPPORTED
 
 
-def _decode(H=32, Hkv=8, d=128, W=4096, ws=None, ws_bytes=0, dt=0):
+def _decode(H=32, Hkv=8, d=128, W=4096, ws=None, ws_bytes=0, dt=0, sink=0, sink_ptr=16):
     p = ctypes.c_void_p(16)
-    return swa.lib().swa_decode(dt, 2, H, Hkv, d, W, p, p, p, p, p, p, p, p, p,
+    sp = ctypes.c_void_p(sink_ptr) if sink_ptr else None
+    return swa.lib().swa_decode(dt, 2, H, Hkv, d, W, sink, sp, sp, p, p, p, p, p, p, p, p, p,
                                 ws, ctypes.c_size_t(ws_bytes), ctypes.c_float(0.1), None)
 
 
@@ -122,4 +129,7 @@ def test_decode_validation_codes():
     assert _decode(ws=ctypes.c_void_p(16), ws_bytes=need - 1) == swa.SWA_EINVAL
     assert _decode(H=48, Hkv=3) == swa.SWA_EUNSUPPORTED  # group of 16
     assert _decode(W=0) == swa.SWA_EINVAL
+    assert _decode(sink=-1) == swa.SWA_EINVAL
+    assert _decode(sink=4, sink_ptr=0) == swa.SWA_EINVAL  # sink caches required
+    assert _decode(sink=4, sink_ptr=8) == swa.SWA_EINVAL  # misaligned
     assert swa.swa_decode_workspace_size(0, 32, 128, 4096) == 0

@@ -76,3 +76,23 @@ def test_random_small_cases():
             rs = rng.integers(0, Wr, size=B)
             both(B, Tq, Tq, W, tq, tk, q_start=p, k_start=p, W_ring=Wr, ring_start=rs,
                  cache_len=cl, next_pos=p)
+
+
+def test_random_small_cases_with_sinks():
+    """Attention sinks ("Sparse attention taxonomy" §3.2): bit-exact metadata
+    against the brute force, with lengths, ragged tiles and sink counts below,
+    at and beyond the window and the length."""
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        B = int(rng.integers(1, 4))
+        W = int(rng.integers(1, 30))
+        S = int(rng.integers(1, 40))
+        tq = int(rng.integers(1, 9))
+        tk = int(rng.integers(1, 9))
+        N = int(rng.integers(1, 70))
+        L = rng.integers(0, N + 1, size=B)
+        both(B, N, N, W, tq, tk, q_len=L, k_len=L, n_sink=S)
+
+
+def test_prefill_workload_with_sinks():
+    both(1, 8192, 8192, 512, 128, 64, n_sink=4)

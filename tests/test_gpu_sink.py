@@ -1,0 +1,153 @@
+"""GPU parity of attention sinks ("Sparse attention taxonomy" §3.2: the first
+tokens stay visible besides the last W) through the C ABI against the fp64
+oracle on the same seeded inputs: the full-sequence forward (and its row
+log-sum-exp), streamed decode with a sink cache, and the backward.  Bars as
+for the plain window (bf16 max-abs 2e-2, mean-abs 2e-3; fp32 1e-4; caches and
+ring state bit-exact; gradients relative to their largest reference value).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_sliding_window_swa_amd as swa
+import oracle
+from causal_sliding_window_swa_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, bf16, where, rel=False):
+    got = f64(got) if torch.is_tensor(got) else got
+    assert np.all(np.isfinite(got)), "non-finite " + where
+    scale = max(1.0, float(np.abs(ref).max())) if rel else 1.0
+    err = np.abs(got - ref) / scale
+    if bf16:
+        assert err.max() <= 2e-2, (where, float(err.max()))
+        assert err.mean() <= 2e-3, (where, float(err.mean()))
+    else:
+        assert err.max() <= 1e-4, (where, float(err.max()))
+
+
+def fwd(inp, W, S, tq, tk, lse=False):
+    q, k, v, ql = inp["q"], inp["k"], inp["v"], inp["q_len"]
+    B, H, N, d = q.shape
+    L = None if ql is None else ql.numpy()
+    meta = swa.swa_blockmask_build(B, N, N, W, tq, tk, q_len=L, k_len=L, n_sink=S)
+    md = swa.meta_to_device(meta, DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    od = torch.full_like(qd, float("nan"))
+    ls = torch.full((B, H, N), float("nan"), device=DEV) if lse else None
+    swa.swa_fwd(qd, kd, vd, od, W, md, q_len=None if ql is None else ql.to(DEV), lse=ls)
+    torch.cuda.synchronize()
+    return od, ls, md
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tq", [128, 64])
+@pytest.mark.parametrize("W,S", [(1, 4), (17, 4), (100, 1), (40, 70), (333, 4)])
+def test_fwd_sink_bf16(d, tq, W, S):
+    inp = synth.gen_fwd(2, 4, 2, 333, d, seed=500 + W + S, std=0.5, len_lo=100, len_hi=333)
+    o, lse, _ = fwd(inp, W, S, tq, 64, lse=True)
+    L = inp["q_len"].numpy()
+    sc = 1 / math.sqrt(d)
+    ref = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), W, sc, q_len=L, n_sink=S)
+    check(o, ref, True, "sink fwd d=%d tq=%d W=%d S=%d" % (d, tq, W, S))
+    _, _, _, rl = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), np.zeros_like(ref), W,
+                             sc, q_len=L, n_sink=S)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(f64(lse)), fin)
+    assert np.max(np.abs(f64(lse)[fin] - rl[fin])) <= 4e-3
+
+
+def test_fwd_sink_fp32():
+    inp = synth.gen_fwd(2, 4, 4, 70, 20, seed=77, std=1.0, dtype="f32", len_lo=30, len_hi=70)
+    for W, S, tq, tk in ((3, 4, 8, 8), (9, 2, 7, 5), (5, 30, 16, 16)):
+        o, _, _ = fwd(inp, W, S, tq, tk)
+        ref = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), W, 1 / math.sqrt(20),
+                         q_len=inp["q_len"].numpy(), n_sink=S)
+        check(o, ref, False, "sink fwd fp32 W=%d S=%d" % (W, S))
+
+
+def test_fwd_sink_prefill_workload_sampled():
+    """The prefill workload (B=1, H=32, N=8192, W=512, d=128) with 4 sinks."""
+    inp = synth.make("prefill")
+    o, _, _ = fwd(inp, 512, 4, 128, 64)
+    rng = np.random.default_rng(9)
+    rows = [[0, int(h), int(i)] for h, i in zip(rng.integers(0, 32, 256),
+                                                 rng.integers(0, 8192, 256))]
+    rows += [[0, 0, 0], [0, 1, 3], [0, 2, 4], [0, 3, 515], [0, 4, 516], [0, 31, 8191]]
+    ref = oracle.fwd_rows(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 512, 1 / math.sqrt(128),
+                          rows, n_sink=4)
+    got = np.stack([f64(o[b, h, i]) for b, h, i in rows])
+    check(got, ref, True, "sink prefill sampled")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("W,S", [(8, 4), (64, 3), (700, 4)])
+def test_decode_sink_stream(dtype, W, S):
+    """Tokens streamed one by one from empty rings: every step's output, the
+    rings, the sink caches and the ring state against the oracle."""
+    d = 128 if dtype == "bf16" else 16
+    B, H, Hkv, T = 3, 8, 2, 40 if W < 100 else 24
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(W * 10 + S)
+    kc = torch.zeros(B, Hkv, W, d, dtype=tdt)
+    vc = torch.zeros(B, Hkv, W, d, dtype=tdt)
+    sk = torch.zeros(B, Hkv, S, d, dtype=tdt)
+    sv = torch.zeros(B, Hkv, S, d, dtype=tdt)
+    rs = torch.tensor([0, 5 % W, W - 1], dtype=torch.int32)
+    cl = torch.zeros(B, dtype=torch.int32)
+    npos = torch.zeros(B, dtype=torch.int32)
+    state = [f64(kc), f64(vc), rs.numpy().copy(), cl.numpy().copy(), npos.numpy().copy(),
+             f64(sk), f64(sv)]
+    dev = [x.to(DEV) for x in (kc, vc, rs, cl, npos, sk, sv)]
+    ws = torch.empty(max(16, swa.swa_decode_workspace_size(B, H, d, W)) // 4 + 4,
+                     dtype=torch.float32, device=DEV)
+    sc = 1 / math.sqrt(d)
+    for step in range(T):
+        q = (torch.randn(B, H, d, generator=gen) * 0.5).to(tdt)
+        kn = (torch.randn(B, Hkv, d, generator=gen) * 0.5).to(tdt)
+        vn = (torch.randn(B, Hkv, d, generator=gen) * 0.5).to(tdt)
+        o = torch.full((B, H, d), float("nan"), dtype=tdt, device=DEV)
+        swa.swa_decode(q.to(DEV), kn.to(DEV), vn.to(DEV), dev[0], dev[1], dev[2], dev[3], dev[4],
+                       o, ws, W, n_sink=S, sink_k=dev[5], sink_v=dev[6])
+        out = oracle.decode(f64(q), f64(kn), f64(vn), state[0], state[1], state[2], state[3],
+                            state[4], W, sc, n_sink=S, sink_k=state[5], sink_v=state[6])
+        ro = out[0]
+        state = [out[1], out[2], out[3], out[4], out[5], out[6], out[7]]
+        torch.cuda.synchronize()
+        check(o, ro, dtype == "bf16", "sink decode %s W=%d S=%d step %d" % (dtype, W, S, step))
+    assert np.array_equal(f64(dev[0]), state[0]) and np.array_equal(f64(dev[1]), state[1])
+    assert np.array_equal(dev[2].cpu().numpy(), state[2])
+    assert np.array_equal(dev[3].cpu().numpy(), state[3])
+    assert np.array_equal(dev[4].cpu().numpy(), state[4])
+    assert np.array_equal(f64(dev[5]), state[5]) and np.array_equal(f64(dev[6]), state[6])
+
+
+@pytest.mark.parametrize("dtype,d,tq,tk", [("bf16", 128, 128, 64), ("bf16", 64, 64, 64),
+                                           ("f32", 12, 8, 8)])
+@pytest.mark.parametrize("W,S", [(17, 4), (100, 1), (30, 90)])
+def test_bwd_sink(dtype, d, tq, tk, W, S):
+    inp = synth.gen_bwd(2, 4, 2, 200, d, seed=600 + W + S, std=0.5 if dtype == "bf16" else 1.0,
+                        dtype=dtype, len_lo=90, len_hi=200)
+    inp["q_len"][0] = 200
+    B, H, N, _ = inp["q"].shape
+    o, lse, md = fwd(inp, W, S, tq, tk, lse=True)
+    qd, kd, vd, dod = (inp[x].to(DEV) for x in ("q", "k", "v", "dout"))
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(swa.swa_bwd_workspace_size(B, H, N) // 4, dtype=torch.float32, device=DEV)
+    swa.swa_bwd(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, W, md, q_len=inp["q_len"].to(DEV))
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"]), W,
+                               1 / math.sqrt(d), q_len=inp["q_len"].numpy(), n_sink=S)
+    bf = dtype == "bf16"
+    check(dq, rq, bf, "sink bwd dq", rel=True)
+    check(dk, rk, bf, "sink bwd dk", rel=True)
+    check(dv, rv, bf, "sink bwd dv", rel=True)
