@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list: prefill,gqa,chunk,decode,bwd")
+    ap.add_argument("--only", default="",
+                    help="comma list: prefill,gqa,chunk,decode,bwd,sink")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(scale for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -77,7 +78,7 @@ def main():
     from causal_sliding_window_swa_amd import synth
 
     only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode",
-                                                         "bwd"}
+                                                         "bwd", "sink"}
     dev = torch.device("cuda:0")
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -164,6 +165,16 @@ def main():
         out["bwd"] = dict(wall_ms=wb, kernel_ms=eb, flops=2.5 * flops)
         log("bwd: wall %.3f ms, event %.3f ms" % (wb, eb))
         del dout, lse, dq, dk, dv, wsb
+
+    # ---------------- prefill with 4 attention sinks -------------
+    if "sink" in only:
+        ms = swa.swa_blockmask_build(B, N, N, W, tq, tk, n_sink=4)
+        mds = swa.meta_to_device(ms, dev)
+        fs = lambda: swa.swa_fwd(q, k, v, o, W, mds)
+        ws_, es_ = timed(fs, K, WU)
+        out["prefill_sink"] = dict(wall_ms=ws_, kernel_ms=es_,
+                                   flops=4.0 * d * ms["valid_pairs"] * H)
+        log("prefill sink: wall %.4f ms, event %.4f ms" % (ws_, es_))
     del inp
 
     # ---------------- GQA prefill with per-sequence lengths -------------
@@ -229,6 +240,17 @@ def main():
         kv_bytes = 2.0 * B5 * Hkv5 * W5 * d5 * 2
         out["decode"] = dict(wall_ms=w5, kernel_ms=e5, kv_bytes=kv_bytes)
         log("decode: wall %.4f ms, event %.4f ms" % (w5, e5))
+        if "sink" in only:  # 4 sinks, all outside the window at these positions
+            sk = torch.zeros(B5, Hkv5, 4, d5, dtype=dv["k_cache"].dtype, device=dev)
+            sv = torch.zeros_like(sk)
+            f6 = lambda: swa.swa_decode(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                        dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                        dv["next_pos"], o5, ws, W5, n_sink=4, sink_k=sk,
+                                        sink_v=sv)
+            w6, e6 = timed(f6, max(10, K), 5)
+            out["decode_sink"] = dict(wall_ms=w6, kernel_ms=e6,
+                                      kv_bytes=kv_bytes + 2.0 * B5 * Hkv5 * 4 * d5 * 2)
+            log("decode sink: wall %.4f ms, event %.4f ms" % (w6, e6))
         del dv
 
     # ---------------- oracle on the host cores -------------
@@ -306,6 +328,20 @@ def main():
                                            "swa_decode", src_digest("swa_decode_bf16.hip")),
                                        "kernel_ms": round(dd["kernel_ms"], 5),
                                        "kernels": "split + combine"}}
+    if "prefill_sink" in out:
+        ps = out["prefill_sink"]
+        t = ps["flops"] / (ps["wall_ms"] * 1e-3) / 1e12
+        line["prefill_sink"] = {"workload": "prefill workload with 4 attention sinks",
+                                "TFLOP_per_s": round(t, 2),
+                                "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                "ms_per_step": round(ps["wall_ms"], 5)}
+    if "decode_sink" in out:
+        ds = out["decode_sink"]
+        gbs = ds["kv_bytes"] / (ds["wall_ms"] * 1e-3) / 1e9
+        line["decode_sink"] = {"workload": "decode workload with 4 attention sinks",
+                               "GB_per_s": round(gbs, 1),
+                               "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                               "ms_per_step": round(ds["wall_ms"], 5)}
     if "bwd" in out:
         bb = out["bwd"]
         t = bb["flops"] / (bb["wall_ms"] * 1e-3) / 1e12
