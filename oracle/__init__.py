@@ -78,6 +78,8 @@ class Oracle:
         lib.orc_bwd_sel_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, d, i, P, P, P, P,
                                          i, P, P, P, P, P]
         lib.orc_bwd_sel_sink.restype = None
+        lib.orc_fwd_varlen.argtypes = [i, i, i, P, i, i, i, P, P, P, d, P]
+        lib.orc_fwd_varlen.restype = None
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -112,6 +114,18 @@ class Oracle:
                                    _ptr(ql), float(scale), rows.shape[0], _ptr(rb), _ptr(rh),
                                    _ptr(ri), _ptr(out))
         return out
+
+    def fwd_varlen(self, q, k, v, cu_seqlens, W: int, scale: float, n_sink: int = 0):
+        """Packed batch: q [total,H,d], k/v [total,Hkv,d] token-major, sequence b
+        owning tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 -> o [total,H,d]."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        cu = _i32(cu_seqlens)
+        total, H, dd = q.shape
+        Hkv = k.shape[1]
+        o = np.zeros_like(q)
+        self.lib.orc_fwd_varlen(len(cu) - 1, H, Hkv, _ptr(cu), dd, W, n_sink, _ptr(q), _ptr(k),
+                                _ptr(v), float(scale), _ptr(o))
+        return o
 
     def bwd(self, q, k, v, dout, W: int, scale: float, q_len=None, n_sink: int = 0):
         """Gradients of the full-sequence forward for output gradient dout.
@@ -238,6 +252,10 @@ def chunk(*a, **kw):
 
 def bwd(*a, **kw):
     return default().bwd(*a, **kw)
+
+
+def fwd_varlen(*a, **kw):
+    return default().fwd_varlen(*a, **kw)
 
 
 def bwd_sel(*a, **kw):

@@ -779,3 +779,44 @@ void orc_bwd_sel(int B, int H, int Hkv, int N, int d, int W, const double *q,
     orc_bwd_sel_sink(B, H, Hkv, N, d, W, 0, q, k, v, dout, q_len, scale, nq_sel, qb, qh, qi,
                      dq_rows, nk_sel, kb_, kg, kj, dk_rows, dv_rows);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Packed variable-length batch ("Dense vs sliding-window sparse attention"
+ * §3.3 calls the varlen kernel with cu_seqlens; §5.2: in a batch the window
+ * is per sequence, and a wrong split lets windows leak across sequences).
+ * Sequence b owns tokens cu[b] .. cu[b+1]-1 of the packed axis; its token i
+ * sits at logical position i and sees only its own sequence's keys, under
+ * the same rule as orc_fwd_sink.  Layout is token-major:
+ * q, o [total][H][d]; k, v [total][Hkv][d]. */
+void orc_fwd_varlen(int B, int H, int Hkv, const int32_t *cu, int d, int W, int S,
+                    const double *q, const double *k, const double *v, double scale,
+                    double *o)
+{
+    const int G = H / Hkv;
+    int b;
+    for (b = 0; b < B; b++) {
+        const int64_t t0 = cu[b];
+        const int len = cu[b + 1] - cu[b];
+        int h;
+        for (h = 0; h < H; h++) {
+            const int64_t g = h / G;
+            int64_t i;
+#pragma omp parallel for schedule(dynamic, 8)
+            for (i = 0; i < len; i++) {
+                const double **kr = malloc(sizeof(*kr) * (size_t)(len > 0 ? len : 1));
+                const double **vr = malloc(sizeof(*vr) * (size_t)(len > 0 ? len : 1));
+                int64_t *kp = malloc(sizeof(*kp) * (size_t)(len > 0 ? len : 1));
+                double *sc = malloc(sizeof(*sc) * (size_t)(len > 0 ? len : 1));
+                int j;
+                for (j = 0; j < len; j++) {
+                    kr[j] = k + ((t0 + j) * Hkv + g) * d;
+                    vr[j] = v + ((t0 + j) * Hkv + g) * d;
+                    kp[j] = j;
+                }
+                attend_row(d, W, S, scale, q + ((t0 + i) * H + h) * d, i, len, kr, vr, kp, sc,
+                           o + ((t0 + i) * H + h) * d);
+                free(kr); free(vr); free(kp); free(sc);
+            }
+        }
+    }
+}

@@ -720,6 +720,39 @@ def pin_sink_bwd(O):
         assert np.array_equal(sk_[r], dk[b, g, j]) and np.array_equal(sv_[r], dv[b, g, j])
 
 
+# ---------------------------------------------------------------------------
+# Packed variable-length batches ("Dense vs sliding-window sparse attention"
+# §3.3 passes cu_seqlens; §5.2: windows are per sequence).
+
+def pin_varlen_equals_per_sequence(O):
+    """A packed batch equals the padded forward of each sequence on its own
+    (exactly), and changing one sequence's K/V leaves every other sequence's
+    output bit-identical (no window crosses a sequence boundary)."""
+    rng = _rng(70)
+    lens = [13, 1, 30, 7, 22]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total, H, Hkv, d = int(cu[-1]), 4, 2, 6
+    q = rng.standard_normal((total, H, d))
+    k = rng.standard_normal((total, Hkv, d))
+    v = rng.standard_normal((total, Hkv, d))
+    for W, S in ((4, 0), (1, 0), (9, 3), (40, 0)):
+        got = O.fwd_varlen(q, k, v, cu, W=W, scale=0.4, n_sink=S)
+        for b, L in enumerate(lens):
+            sl = slice(int(cu[b]), int(cu[b + 1]))
+            ref = O.fwd(q[sl].transpose(1, 0, 2)[None], k[sl].transpose(1, 0, 2)[None],
+                        v[sl].transpose(1, 0, 2)[None], W=W, scale=0.4, n_sink=S)
+            assert np.array_equal(got[sl], ref[0].transpose(1, 0, 2)), (W, S, b)
+    base = O.fwd_varlen(q, k, v, cu, W=5, scale=0.4)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[2]:cu[3]] += 3.0
+    v2[cu[2]:cu[3]] -= 2.0
+    got = O.fwd_varlen(q, k2, v2, cu, W=5, scale=0.4)
+    keep = np.ones(total, dtype=bool)
+    keep[cu[2]:cu[3]] = False
+    assert np.array_equal(got[keep], base[keep])
+    assert not np.array_equal(got[~keep], base[~keep])
+
+
 PINS = [
     pin_window_visible_sets,
     pin_pair_counts,
@@ -747,4 +780,5 @@ PINS = [
     pin_sink_mask_sdpa,
     pin_sink_decode_streams_like_full,
     pin_sink_bwd,
+    pin_varlen_equals_per_sequence,
 ]

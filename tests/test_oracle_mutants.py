@@ -50,6 +50,10 @@ MUTANTS = {
     "sink_not_causal": ("(kpos < S && kpos <= qpos)", "(kpos < S)"),
     "sink_decode_double_count": ("nsink = (int)(S < oldest ? S : oldest);", "nsink = S;"),
     "sink_cache_not_written": ("if (S > 0 && next_pos[b] < S) {", "if (S > 0 && next_pos[b] < 0) {"),
+    "varlen_key_from_previous_sequence": ("kr[j] = k + ((t0 + j) * Hkv + g) * d;",
+                                          "kr[j] = k + ((t0 + j - (j == 0 && t0 > 0)) * Hkv + g) * d;"),
+    "varlen_query_position_global": ("attend_row(d, W, S, scale, q + ((t0 + i) * H + h) * d, i, len,",
+                                     "attend_row(d, W, S, scale, q + ((t0 + i) * H + h) * d, t0 + i, len,"),
     "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
                           "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
 }
