@@ -10,6 +10,7 @@ Functions keep the ABI's names:
     swa_blockmask_size(B, nq, nk, tile_q, tile_k)          -> (cls_elems, max_nnz)
     swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, ..., n_sink=0) -> dict (host numpy)
     swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None)
+    swa_fwd_varlen(q, k, v, o, W, meta, cu_seqlens, lse=None, scale=None)
     swa_bwd_workspace_size(B, H, N)
     swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, scale=None)
     swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len,
@@ -43,7 +44,7 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 # Symbols declared in include/swa.h (checked by the CPU tests).
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
            "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
-           "swa_last_error")
+           "swa_fwd_varlen", "swa_last_error")
 
 
 class SwaError(RuntimeError):
@@ -75,6 +76,8 @@ def lib():
             L.swa_blockmask_build.argtypes = [I, I, I, I, I, I, I, P, P, P, P, I, P, P, P,
                                               P, P, P, P, ctypes.POINTER(MaskStats)]
             L.swa_fwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, P]
+            L.swa_fwd_varlen.argtypes = [I, I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
+                                         P, F, P]
             L.swa_bwd_workspace_size.argtypes = [I, I, I]
             L.swa_bwd_workspace_size.restype = ctypes.c_size_t
             L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -88,7 +91,7 @@ def lib():
             L.swa_last_error.argtypes = []
             L.swa_last_error.restype = ctypes.c_char_p
             for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
-                      "swa_prefill_chunk", "swa_decode", "swa_bwd"):
+                      "swa_prefill_chunk", "swa_decode", "swa_bwd", "swa_fwd_varlen"):
                 getattr(L, n).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -144,7 +147,7 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
     nnz = int(row_ptr[-1])
     out = {"cls": cls[:cls_n].reshape(B, nqt, nkt), "row_ptr": row_ptr,
            "col": col[:nnz].copy(), "col_cls": col_cls[:nnz].copy(),
-           "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink}
+           "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink, "max_len": nq}
     out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
     return out
 
@@ -160,7 +163,7 @@ def meta_to_device(meta, device):
             "col_cls": torch.from_numpy(ccls).to(dev),
             "cls": torch.from_numpy(np.ascontiguousarray(meta["cls"]).reshape(-1)).to(dev),
             "tile_q": meta["tile_q"], "tile_k": meta["tile_k"],
-            "n_sink": meta.get("n_sink", 0)}
+            "n_sink": meta.get("n_sink", 0), "max_len": meta.get("max_len", 0)}
 
 
 def _dptr(t):
@@ -204,6 +207,29 @@ def swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None, stream=None):
                          _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(q_len),
                          _dptr(meta["row_ptr"]), _dptr(meta["col"]), _dptr(meta["col_cls"]),
                          _dptr(lse), ctypes.c_float(scale), _stream(q, stream)))
+    return o
+
+
+def swa_fwd_varlen(q, k, v, o, W, meta, cu_seqlens, lse=None, scale=None, stream=None):
+    """Packed variable-length forward.  q,o [total,H,d], k,v [total,Hkv,d]
+    token-major device tensors; cu_seqlens int32 [B+1] device tensor; meta
+    built with nq = nk_lin = max_len and q_len = k_len = the lengths;
+    lse: optional fp32 [total,H] device tensor."""
+    for t in (q, k, v, o):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (total, Hkv, d) and tuple(v.shape) == (total, Hkv, d) and
+             tuple(o.shape) == (total, H, d), "shape mismatch")
+    _require(k.dtype == q.dtype == v.dtype == o.dtype, "dtype mismatch")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().swa_fwd_varlen(_dtype_code(q), B, H, Hkv, total, meta["max_len"], d, W,
+                                meta.get("n_sink", 0), meta["tile_q"], meta["tile_k"],
+                                _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(cu_seqlens),
+                                _dptr(meta["row_ptr"]), _dptr(meta["col"]),
+                                _dptr(meta["col_cls"]), _dptr(lse), ctypes.c_float(scale),
+                                _stream(q, stream)))
     return o
 
 

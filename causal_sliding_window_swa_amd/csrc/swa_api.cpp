@@ -116,6 +116,45 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
 }
 
+extern "C" int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len,
+                              int d, int W, int n_sink, int tile_q, int tile_k, const void *q,
+                              const void *k, const void *v, void *o,
+                              const int32_t *cu_seqlens_dev, const int32_t *row_ptr_dev,
+                              const int32_t *col_dev, const uint8_t *col_cls_dev,
+                              float *lse_dev, float scale, void *stream) {
+    static const char *fn = "swa_fwd_varlen";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
+    if (total < 1 || max_len < 1 || max_len > total)
+        return fail(SWA_EINVAL, "%s: need 1 <= max_len <= total (total=%d max_len=%d)", fn,
+                    total, max_len);
+    if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
+    const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
+    if ((rc = check_ptrs(fn, ptrs, names, 6))) return rc;
+    if (!col_cls_dev || !cu_seqlens_dev)
+        return fail(SWA_EINVAL, "%s: col_cls and cu_seqlens are required", fn);
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+
+    swa::AttnArgs a = {};
+    a.mode = 0;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.nq = max_len; a.d = d; a.W = W;
+    a.tile_q = tile_q; a.tile_k = tile_k;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.cu = cu_seqlens_dev;
+    a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.lse = lse_dev;
+    a.n_sink = n_sink;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
+}
+
 extern "C" size_t swa_bwd_workspace_size(int B, int H, int N) {
     if (B < 1 || H < 1 || N < 1) return 0;
     return (size_t)B * H * N * sizeof(float);

@@ -59,21 +59,28 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
     const int g = h / (a.H / a.Hkv);
     const int nqt = (nq + a.tile_q - 1) / a.tile_q;
     const int nk = (MODE == 1 ? W : 0) + nq;
-    const int qlen = (MODE == 0) ? (a.q_len ? a.q_len[b] : nq) : nq;
+    // packed batch: sequence b owns tokens cu[b] .. cu[b+1]-1 (token-major)
+    const bool pk = MODE == 0 && a.cu;
+    const int cub = pk ? a.cu[b] : 0;
+    const int nrows = pk ? a.cu[b + 1] - cub : nq;
+    const int qlen = pk ? nrows : ((MODE == 0) ? (a.q_len ? a.q_len[b] : nq) : nq);
     const int rs = (MODE == 1) ? a.ring_start[b] : 0;
     const int cl = (MODE == 1) ? a.cache_len[b] : 0;
     const int np = (MODE == 1) ? a.next_pos[b] : 0;
     const size_t kvh = (size_t)b * a.Hkv + g;
-    const float *klin = (const float *)a.k + kvh * nq * d;
-    const float *vlin = (const float *)a.v + kvh * nq * d;
+    // linear key row t: kvh row t, or token cub + t in the packed layout
+    const size_t krs = pk ? (size_t)a.Hkv * d : (size_t)d;
+    const float *klin = (const float *)a.k + (pk ? ((size_t)cub * a.Hkv + g) * d : kvh * nq * d);
+    const float *vlin = (const float *)a.v + (pk ? ((size_t)cub * a.Hkv + g) * d : kvh * nq * d);
     const float *kring = (MODE == 1) ? (const float *)a.kc + kvh * W * d : nullptr;
     const float *vring = (MODE == 1) ? (const float *)a.vc + kvh * W * d : nullptr;
     const int e0 = a.row_ptr[b * nqt + qt], e1 = a.row_ptr[b * nqt + qt + 1];
-    const int i_end = min(nq, (qt + 1) * a.tile_q);
+    const int i_end = min(nrows, (qt + 1) * a.tile_q);
 
     for (int i = qt * a.tile_q + threadIdx.x; i < i_end; i += 64) {
-        const float *qrow = (const float *)a.q + (((size_t)b * a.H + h) * nq + i) * d;
-        float *orow = (float *)a.o + (((size_t)b * a.H + h) * nq + i) * d;
+        const size_t ridx = pk ? (size_t)(cub + i) * a.H + h : ((size_t)b * a.H + h) * nq + i;
+        const float *qrow = (const float *)a.q + ridx * d;
+        float *orow = (float *)a.o + ridx * d;
         RowState<DMAX> st;
         st.init(qrow, d);
         const int qpos = ((MODE == 1) ? np : 0) + i;
@@ -96,8 +103,8 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
                         const int t = j - (MODE == 1 ? W : 0);
                         pos = ((MODE == 1) ? np : 0) + t;
                         ok = (MODE == 1) ? true : (t < qlen);
-                        kr = klin + (size_t)t * d;
-                        vr = vlin + (size_t)t * d;
+                        kr = klin + (size_t)t * krs;
+                        vr = vlin + (size_t)t * krs;
                     }
                     if (ok && pos <= qpos && (pos >= qpos - W + 1 || pos < a.n_sink))
                         st.add(kr, vr, d, a.scale);
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
             }
         }
         st.store(orow, d);
-        if (MODE == 0 && a.lse) a.lse[((size_t)b * a.H + h) * nq + i] = st.lse();
+        if (MODE == 0 && a.lse) a.lse[ridx] = st.lse();
     }
 }
 

@@ -28,6 +28,9 @@ struct AttnArgs {
     const uint8_t *col_cls;
     float *lse;  // mode 0, may be null: [B][H][nq] natural-log row log-sum-exp
     int n_sink;  // mode 0: keys at positions < n_sink stay visible (attention sinks)
+    const int32_t *cu;  // mode 0, may be null: packed batch, sequence b = tokens
+                        // cu[b] .. cu[b+1]-1 of token-major q, o [tokens][H][d],
+                        // k, v [tokens][Hkv][d]; nq is then the longest sequence
     float scale;
 };
 

@@ -84,7 +84,7 @@ __device__ __forceinline__ int xcd_remap(int p, int T) {
     return x * q + (x < r ? x : r) + i;
 }
 
-template <int MODE, int D, int NW>
+template <int MODE, int D, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tile_kernel(AttnArgs a) {
     constexpr int KS = D / 16;          // k-steps of the QK product
@@ -119,7 +119,11 @@ void tile_kernel(AttnArgs a) {
     kp.nq = nq;
     kp.W = a.W;
     kp.nrt = (MODE == 1) ? a.W / BN : 0;
-    kp.qlen = (MODE == 0) ? (a.q_len ? a.q_len[b] : nq) : nq;
+    // packed batch (PK): sequence b owns tokens cu[b] .. cu[b+1]-1 of a
+    // token-major [tokens][heads][D] layout; only its own rows exist
+    const int cub = PK ? a.cu[b] : 0;
+    const int nrows = PK ? a.cu[b + 1] - cub : nq;
+    kp.qlen = PK ? nrows : ((MODE == 0) ? (a.q_len ? a.q_len[b] : nq) : nq);
     kp.rs = (MODE == 1) ? a.ring_start[b] : 0;
     kp.cl = (MODE == 1) ? a.cache_len[b] : 0;
     kp.np = (MODE == 1) ? a.next_pos[b] : 0;
@@ -131,10 +135,12 @@ void tile_kernel(AttnArgs a) {
     const int myrow = row0 + lq;
     bf16x8 qf[KS];
     {
-        const __bf16 *qp = (const __bf16 *)a.q + (((size_t)b * a.H + h) * nq + myrow) * D;
+        const __bf16 *qp = (const __bf16 *)a.q +
+                           (PK ? ((size_t)(cub + myrow) * a.H + h) * D
+                               : (((size_t)b * a.H + h) * nq + myrow) * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
-            u32x4 x = (myrow < nq) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+            u32x4 x = (myrow < nrows) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -142,8 +148,12 @@ void tile_kernel(AttnArgs a) {
     // ---- key/value rows of a tile (rows past the data are clamped to a real
     // row: they are always masked, and their values stay finite)
     const size_t kvh = (size_t)b * a.Hkv + g;
-    const __bf16 *klin = (const __bf16 *)a.k + kvh * (size_t)nq * D;
-    const __bf16 *vlin = (const __bf16 *)a.v + kvh * (size_t)nq * D;
+    // global row stride in bytes: D*2, or Hkv*D*2 in the packed layout
+    const int RSB = PK ? a.Hkv * ROWB : ROWB;
+    const __bf16 *klin = (const __bf16 *)a.k + (PK ? ((size_t)cub * a.Hkv + g) * D
+                                                   : kvh * (size_t)nq * D);
+    const __bf16 *vlin = (const __bf16 *)a.v + (PK ? ((size_t)cub * a.Hkv + g) * D
+                                                   : kvh * (size_t)nq * D);
     const __bf16 *kring = (MODE == 1) ? (const __bf16 *)a.kc + kvh * (size_t)a.W * D : nullptr;
     const __bf16 *vring = (MODE == 1) ? (const __bf16 *)a.vc + kvh * (size_t)a.W * D : nullptr;
     // swizzles: logical 16-byte chunk c of row r sits at physical chunk c ^ swz(r)
@@ -156,16 +166,18 @@ void tile_kernel(AttnArgs a) {
     for (int i = 0; i < LPW; i++) {
         const int r = (wave * LPW + i) * RPL + lane / CPR;
         const int pch = lane % CPR;
-        koff[i] = (uint32_t)(r * ROWB + (pch ^ kswz(r)) * 16);
-        voff[i] = (uint32_t)(r * ROWB + (pch ^ vswz(r)) * 16);
+        koff[i] = (uint32_t)(r * RSB + (pch ^ kswz(r)) * 16);
+        voff[i] = (uint32_t)(r * RSB + (pch ^ vswz(r)) * 16);
     }
     auto issue = [&](int kt, char *kdst) {
         char *vdst = kdst + TILEB;
         const bool ring = (MODE == 1) && kt < kp.nrt;
         const int t0 = ring ? kt * BN : (kt - kp.nrt) * BN;  // first row of the tile
-        const char *kb = (const char *)((ring ? kring : klin) + (size_t)t0 * D);
-        const char *vb = (const char *)((ring ? vring : vlin) + (size_t)t0 * D);
-        if (ring || t0 + BN <= nq) {
+        const char *kb = ring ? (const char *)(kring + (size_t)t0 * D)
+                              : (const char *)klin + (size_t)t0 * RSB;
+        const char *vb = ring ? (const char *)(vring + (size_t)t0 * D)
+                              : (const char *)vlin + (size_t)t0 * RSB;
+        if (ring || t0 + BN <= nrows) {
 #pragma unroll
             for (int i = 0; i < LPW; i++) {
                 const int ins = wave * LPW + i;
@@ -179,10 +191,10 @@ void tile_kernel(AttnArgs a) {
             for (int i = 0; i < LPW; i++) {
                 const int ins = wave * LPW + i;
                 const int r = ins * RPL + lane / CPR;
-                const int rc = (t0 + r < nq) ? r : nq - 1 - t0;  // 0 <= rc < nq - t0
+                const int rc = (t0 + r < nrows) ? r : nrows - 1 - t0;  // 0 <= rc < nrows - t0
                 // same chunk, row rc: a non-negative offset inside the data
-                const int ko = (int)koff[i] + (rc - r) * ROWB;
-                const int vo = (int)voff[i] + (rc - r) * ROWB;
+                const int ko = (int)koff[i] + (rc - r) * RSB;
+                const int vo = (int)voff[i] + (rc - r) * RSB;
                 __builtin_amdgcn_global_load_lds((const void *)(kb + ko),
                                                  (void *)(kdst + ins * 1024), 16, 0, 0);
                 __builtin_amdgcn_global_load_lds((const void *)(vb + vo),
@@ -205,7 +217,7 @@ void tile_kernel(AttnArgs a) {
     const int e0 = a.row_ptr[mrow], e1 = a.row_ptr[mrow + 1];
     const int qpos = qbase + myrow;
     const bool qvalid = myrow < qlen;
-    const int nlin_full = nq / BN;  // linear tiles lying fully inside the data
+    const int nlin_full = nrows / BN;  // linear tiles lying fully inside the data
 
     // per-lane constants of the two LDS read patterns
     const int kr_row = lq;                       // + kb*32
@@ -414,12 +426,13 @@ void tile_kernel(AttnArgs a) {
     // ---- epilogue: O = O / l; rows without any visible key (padding) get 0.
     // The row log-sum-exp (natural log) of the scaled scores is
     // (m_ref + log2 l) * ln 2, since l = sum exp2(s*c2 - m_ref).
-    if (myrow < nq) {
+    if (myrow < nrows) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
         if (MODE == 0 && a.lse && hh == 0)
-            a.lse[((size_t)b * a.H + h) * nq + myrow] =
+            a.lse[PK ? (size_t)(cub + myrow) * a.H + h : ((size_t)b * a.H + h) * nq + myrow] =
                 (l_run > 0.f) ? (m_ref + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-        __bf16 *op = (__bf16 *)a.o + (((size_t)b * a.H + h) * nq + myrow) * D;
+        __bf16 *op = (__bf16 *)a.o + (PK ? ((size_t)(cub + myrow) * a.H + h) * D
+                                         : (((size_t)b * a.H + h) * nq + myrow) * D);
 #pragma unroll
         for (int db = 0; db < DB; db++)
 #pragma unroll
@@ -437,7 +450,12 @@ hipError_t launch_one(const AttnArgs &a, hipStream_t s) {
     const long nqt = (a.nq + 32 * NW - 1) / (32 * NW);
     const long total = nqt * a.H * a.B;
     if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((tile_kernel<MODE, D, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, a);
+    if (MODE == 0 && a.cu)
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true>), dim3((unsigned)total), dim3(NW * 64),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false>), dim3((unsigned)total),
+                           dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -135,6 +135,26 @@ int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
             const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *col_cls_dev,
             float *lse_dev, float scale, void *stream);
 
+/* Full-sequence forward of a packed variable-length batch [Blog §3.3 passes
+ * cu_seqlens to the varlen kernel; §5.2: the window is per sequence, and a
+ * wrong split lets windows leak across sequences].  Sequence b owns tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of the packed axis (token i of it at
+ * logical position i); layout is token-major: q, o [total][H][d], k, v
+ * [total][Hkv][d]; lse_dev (may be NULL) [total][H].  cu_seqlens_dev: device
+ * int32 [B+1] with cu[0] = 0, non-decreasing, cu[B] = total and every length
+ * at most max_len.  Metadata: swa_blockmask_build with nq = nk_lin = max_len,
+ * q_len = k_len = the lengths (host copy), the call's W, n_sink and tiles.
+ * No padding is read or written.  The kernel does not re-check cu_seqlens
+ * against the metadata: inconsistent ones are a caller error.
+ * Supported and errors: as swa_fwd (max_len in place of N), plus SWA_EINVAL
+ * for total < 1, max_len outside [1, total] or NULL cu_seqlens_dev. */
+int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len, int d, int W,
+                   int n_sink, int tile_q, int tile_k,
+                   const void *q, const void *k, const void *v, void *o,
+                   const int32_t *cu_seqlens_dev,
+                   const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *col_cls_dev,
+                   float *lse_dev, float scale, void *stream);
+
 /* Bytes of device workspace swa_bwd needs (fp32 row values [B][H][N]);
  * 0 for non-positive sizes. */
 size_t swa_bwd_workspace_size(int B, int H, int N);

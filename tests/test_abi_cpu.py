@@ -100,6 +100,21 @@ def test_bwd_validation_codes():
     assert _bwd(cls=False) == swa.SWA_EINVAL
 
 
+def _varlen(total=100, max_len=60, cu=True, d=128, W=16):
+    p = ctypes.c_void_p(16)
+    return swa.lib().swa_fwd_varlen(0, 2, 4, 2, total, max_len, d, W, 0, 128, 64, p, p, p, p,
+                                    p if cu else None, p, p, p, None, ctypes.c_float(0.1), None)
+
+
+def test_varlen_validation_codes():
+    assert _varlen(total=0) == swa.SWA_EINVAL
+    assert _varlen(max_len=0) == swa.SWA_EINVAL
+    assert _varlen(max_len=101) == swa.SWA_EINVAL
+    assert _varlen(cu=False) == swa.SWA_EINVAL
+    assert _varlen(W=0) == swa.SWA_EINVAL
+    assert _varlen(d=96) == swa.SWA_EUNSUPPORTED
+
+
 def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False):
     p = ctypes.c_void_p(16)
     st = None if nullstate else p
