@@ -192,7 +192,19 @@ def main():
         w3, e3 = timed(f3, max(3, K // 10), 2)
         out["gqa"] = dict(wall_ms=w3, kernel_ms=e3, flops=4.0 * d3 * m3["valid_pairs"] * H3)
         log("gqa: wall %.3f ms, event %.3f ms" % (w3, e3))
+        # the same sequences packed token-major without padding (swa_fwd_varlen)
+        lens = [int(x) for x in L]
+        pk = [torch.cat([t[b, :, :n].transpose(0, 1) for b, n in enumerate(lens)]).contiguous()
+              for t in (q3, k3, v3)]
         del q3, k3, v3, o3
+        cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+        op = torch.empty_like(pk[0])
+        f3p = lambda: swa.swa_fwd_varlen(pk[0], pk[1], pk[2], op, 4096, md3, cu)
+        w3p, e3p = timed(f3p, max(3, K // 10), 2)
+        out["gqa_packed"] = dict(wall_ms=w3p, kernel_ms=e3p, flops=out["gqa"]["flops"],
+                                 tokens=int(sum(lens)))
+        log("gqa packed: wall %.3f ms, event %.3f ms" % (w3p, e3p))
+        del pk, op
 
     # ---------------- chunked prefill against the ring -------------
     if "chunk" in only:
@@ -358,6 +370,15 @@ def main():
                                "TFLOP_per_s": round(t, 2),
                                "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                "ms_per_step": round(g3["wall_ms"], 4)}
+    if "gqa_packed" in out:
+        gp = out["gqa_packed"]
+        t = gp["flops"] / (gp["wall_ms"] * 1e-3) / 1e12
+        line["prefill_gqa_packed"] = {"workload": "the GQA workload's sequences packed "
+                                                  "token-major (cu_seqlens, %d tokens, no "
+                                                  "padding)" % gp["tokens"],
+                                      "TFLOP_per_s": round(t, 2),
+                                      "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                      "ms_per_step": round(gp["wall_ms"], 4)}
     if "chunk" in out:
         c4 = out["chunk"]
         t = c4["flops"] / (c4["wall_ms"] * 1e-3) / 1e12
