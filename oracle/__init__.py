@@ -80,6 +80,13 @@ class Oracle:
         lib.orc_bwd_sel_sink.restype = None
         lib.orc_fwd_varlen.argtypes = [i, i, i, P, i, i, i, P, P, P, d, P]
         lib.orc_fwd_varlen.restype = None
+        L = ctypes.c_int64
+        lib.orc_layer_plan.argtypes = [i, i, i, P, P, P]
+        lib.orc_layer_plan.restype = None
+        lib.orc_cache_bytes.argtypes = [L] * 8
+        lib.orc_cache_bytes.restype = L
+        lib.orc_cache_bytes_layers.argtypes = [L, L, L, L, L, i, P]
+        lib.orc_cache_bytes_layers.restype = L
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -114,6 +121,23 @@ class Oracle:
                                    _ptr(ql), float(scale), rows.shape[0], _ptr(rb), _ptr(rh),
                                    _ptr(ri), _ptr(out))
         return out
+
+    def layer_plan(self, L: int, a: int, b: int):
+        """Windowed (1) / global (0) flag per layer for the repeating a:b
+        pattern, and the counts (L_s, L_f)."""
+        flags = np.zeros(max(1, L), dtype=np.uint8)
+        ns, nf = ctypes.c_int(0), ctypes.c_int(0)
+        self.lib.orc_layer_plan(L, a, b, _ptr(flags), ctypes.byref(ns), ctypes.byref(nf))
+        return flags[:L].copy(), ns.value, nf.value
+
+    def cache_bytes(self, B, G, d, s, T, W, L_s, L_f) -> int:
+        """The pages' estimate 2BGds[L_s min(T,W) + L_f T] in bytes."""
+        return int(self.lib.orc_cache_bytes(B, G, d, s, T, W, L_s, L_f))
+
+    def cache_bytes_layers(self, B, G, d, s, T, W_layer) -> int:
+        """Sum over layers of 2BGds min(T, W_l), W_l = -1 for a global layer."""
+        w = np.ascontiguousarray(np.asarray(W_layer, dtype=np.int32))
+        return int(self.lib.orc_cache_bytes_layers(B, G, d, s, T, w.size, _ptr(w)))
 
     def fwd_varlen(self, q, k, v, cu_seqlens, W: int, scale: float, n_sink: int = 0):
         """Packed batch: q [total,H,d], k/v [total,Hkv,d] token-major, sequence b
@@ -268,3 +292,15 @@ def decode(*a, **kw):
 
 def blockmask(*a, **kw):
     return default().blockmask(*a, **kw)
+
+
+def layer_plan(*a, **kw):
+    return default().layer_plan(*a, **kw)
+
+
+def cache_bytes(*a, **kw):
+    return default().cache_bytes(*a, **kw)
+
+
+def cache_bytes_layers(*a, **kw):
+    return default().cache_bytes_layers(*a, **kw)

@@ -820,3 +820,58 @@ void orc_fwd_varlen(int B, int H, int Hkv, const int32_t *cu, int d, int W, int 
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Persistent KV-cache size over a stack of layers [Ch10 §10.2].
+ *
+ * A windowed layer keeps at most its last W positions of K and V, so after T
+ * tokens it holds min(T, W) rows per KV head; a full-history (global) layer
+ * holds all T.  With L_s windowed and L_f global layers the pages estimate
+ *     2 * B * G * d * s * [ L_s * min(T, W) + L_f * T ]      bytes
+ * (G KV heads, s bytes per element, the 2 for K and V).  The counts must be
+ * whole layers: the pages warn that a ratio such as 5:1 is not itself a
+ * layer count.
+ * READING (the pages only say the ratio is resolved into whole layers, and
+ * that a stride option picks the windowed layers): the ratio a:b is a
+ * repeating period of a windowed layers followed by b global ones, from
+ * layer 0 upward; a stack of L layers takes the first L layers of that
+ * pattern.
+ * READING: a window of -1 marks a global layer, as a (-1, -1) window means
+ * dense attention in [Blog §3.3].
+ * --------------------------------------------------------------------------- */
+
+/* Layer l of the repeating a:b pattern is windowed (1) or global (0). */
+void orc_layer_plan(int L, int a, int b, uint8_t *is_local, int *L_s, int *L_f)
+{
+    int l, ns = 0, nf = 0;
+    for (l = 0; l < L; l++) {
+        const int local = (l % (a + b)) < a;
+        is_local[l] = (uint8_t)local;
+        if (local) ns++; else nf++;
+    }
+    *L_s = ns;
+    *L_f = nf;
+}
+
+/* The pages' estimate with one window W for every windowed layer. */
+int64_t orc_cache_bytes(int64_t B, int64_t G, int64_t d, int64_t s, int64_t T, int64_t W,
+                        int64_t L_s, int64_t L_f)
+{
+    const int64_t kept = T < W ? T : W;
+    return 2 * B * G * d * s * (L_s * kept + L_f * T);
+}
+
+/* The same count layer by layer, each layer with its own window W_layer[l]
+ * (-1 = global), as in the per-layer window tip of [Blog §3.1]. */
+int64_t orc_cache_bytes_layers(int64_t B, int64_t G, int64_t d, int64_t s, int64_t T, int L,
+                               const int32_t *W_layer)
+{
+    int64_t total = 0;
+    int l;
+    for (l = 0; l < L; l++) {
+        const int64_t w = W_layer[l];
+        const int64_t kept = (w < 0 || T < w) ? T : w;
+        total += 2 * B * G * d * s * kept;
+    }
+    return total;
+}

@@ -753,6 +753,80 @@ def pin_varlen_equals_per_sequence(O):
     assert not np.array_equal(got[~keep], base[~keep])
 
 
+def pin_cache_dense_example(O):
+    """[Blog §2.1] prints the dense KV cache of a 32-layer, 32-head, d=128
+    fp16 model at t=8192: one K about 67 MB, K+V about 134 MB per layer,
+    about 4.3 GB over the layers.  Dense layers are global layers of the
+    estimate ([Ch10 §10.2] with L_s = 0)."""
+    g = gold("blog_dense_kv_cache.json")
+    B, G, d, s, T, L = (g[k] for k in ("B", "heads", "head_dim", "bytes_per_element", "t",
+                                       "layers"))
+    one_layer = O.cache_bytes(B, G, d, s, T, 1, 0, 1)
+    assert round(one_layer / 2 / 1e6) == g["one_K_MB"], one_layer
+    assert round(one_layer / 1e6) == g["K_plus_V_per_layer_MB"], one_layer
+    total = O.cache_bytes(B, G, d, s, T, 1, 0, L)
+    assert round(total / 1e9, 1) == g["all_layers_GB"], total
+    assert O.cache_bytes_layers(B, G, d, s, T, [-1] * L) == total
+    # a window at least as long as the text changes nothing [Ch10 §10.2]
+    assert O.cache_bytes(B, G, d, s, T, T, L, 0) == total
+    assert O.cache_bytes_layers(B, G, d, s, T, [T + 5] * L) == total
+
+
+def pin_cache_window_bound(O):
+    """[Ch10 §10.2]: a windowed layer keeps at most its last W positions, a
+    per-layer bound of 2BWGds bytes once T >= W.  Checked against the byte
+    size of the ring cache tensors themselves (numpy nbytes of [B,G,W,d]
+    arrays, K and V): at B=64, G=8, W=4096, d=128 in bf16 that is the
+    1 073 741 824 bytes one decode step reads.  Below W tokens the layer
+    holds only T rows, like a global layer."""
+    B, G, W, d = 64, 8, 4096, 128
+    ring = 2 * np.zeros((B, G, W, d), dtype=np.float16).nbytes
+    assert ring == 1073741824
+    for T in (W, W + 1, 131072):
+        assert O.cache_bytes(B, G, d, 2, T, W, 1, 0) == ring
+        assert O.cache_bytes_layers(B, G, d, 2, T, [W]) == ring
+    for T in (0, 1, 77, W - 1):
+        part = 2 * np.zeros((B, G, T, d), dtype=np.float16).nbytes
+        assert O.cache_bytes(B, G, d, 2, T, W, 1, 0) == part
+        assert O.cache_bytes(B, G, d, 2, T, W, 0, 1) == part
+        assert O.cache_bytes_layers(B, G, d, 2, T, [W, -1]) == 2 * part
+    # linear in each of B, G, d, s and in the layer counts
+    base = O.cache_bytes(3, 5, 7, 1, 1000, 300, 2, 3)
+    assert base == 2 * O.cache_bytes(3, 5, 7, 1, 1000, 300, 1, 0) + \
+        3 * O.cache_bytes(3, 5, 7, 1, 1000, 300, 0, 1)
+    assert O.cache_bytes(3, 5, 7, 4, 1000, 300, 2, 3) == 4 * base
+    assert O.cache_bytes(6, 5, 7, 1, 1000, 300, 2, 3) == 2 * base
+
+
+def pin_layer_plan(O):
+    """[Ch10 §10.2]: a local:global ratio is resolved into whole layers.
+    The pattern is checked against numpy's tile of one period; the counts
+    against L*a/(a+b) when the period divides L, and against the example of
+    26 layers at 5:1 (22 + 4, where 26*5/6 is not a whole number)."""
+    for L, a, b in [(26, 5, 1), (12, 1, 1), (32, 3, 1), (7, 2, 3), (5, 0, 1), (5, 1, 0),
+                    (1, 5, 1), (0, 2, 2), (40, 1, 7)]:
+        flags, ns, nf = O.layer_plan(L, a, b)
+        ref = np.tile(np.array([1] * a + [0] * b, dtype=np.uint8), L // (a + b) + 1)[:L]
+        assert np.array_equal(flags, ref), (L, a, b)
+        assert ns + nf == L and ns == int(ref.sum())
+        if L % (a + b) == 0:
+            assert ns * (a + b) == L * a
+    assert O.layer_plan(26, 5, 1)[1:] == (22, 4)
+    # the plan's counts in the one-W estimate equal the per-layer sum
+    flags, ns, nf = O.layer_plan(26, 5, 1)
+    W_layer = np.where(flags == 1, 1024, -1)
+    for T in (100, 1024, 5000):
+        assert O.cache_bytes_layers(2, 8, 128, 2, T, W_layer) == \
+            O.cache_bytes(2, 8, 128, 2, T, 1024, ns, nf)
+    # [Blog §3.1]: per-layer windows (12 layers at 256, 8 at 512, 12 at 1024)
+    # are the sum of three single-window stacks
+    bands = [256] * 12 + [512] * 8 + [1024] * 12
+    for T in (200, 700, 4096):
+        assert O.cache_bytes_layers(1, 32, 128, 2, T, bands) == sum(
+            O.cache_bytes(1, 32, 128, 2, T, w, n, 0) for w, n in ((256, 12), (512, 8),
+                                                                   (1024, 12)))
+
+
 PINS = [
     pin_window_visible_sets,
     pin_pair_counts,
@@ -781,4 +855,7 @@ PINS = [
     pin_sink_decode_streams_like_full,
     pin_sink_bwd,
     pin_varlen_equals_per_sequence,
+    pin_cache_dense_example,
+    pin_cache_window_bound,
+    pin_layer_plan,
 ]

@@ -54,6 +54,17 @@ MUTANTS = {
                                           "kr[j] = k + ((t0 + j - (j == 0 && t0 > 0)) * Hkv + g) * d;"),
     "varlen_query_position_global": ("attend_row(d, W, S, scale, q + ((t0 + i) * H + h) * d, i, len,",
                                      "attend_row(d, W, S, scale, q + ((t0 + i) * H + h) * d, t0 + i, len,"),
+    "cache_kv_factor_dropped": ("return 2 * B * G * d * s * (L_s * kept + L_f * T);",
+                                "return B * G * d * s * (L_s * kept + L_f * T);"),
+    "cache_window_not_clipped": ("const int64_t kept = T < W ? T : W;",
+                                 "const int64_t kept = W;"),
+    "cache_layers_global_ignored": ("const int64_t kept = (w < 0 || T < w) ? T : w;",
+                                    "const int64_t kept = (T < w) ? T : (w < 0 ? 0 : w);"),
+    "layer_plan_global_first": ("const int local = (l % (a + b)) < a;",
+                                "const int local = (l % (a + b)) >= b;"),
+    "layer_plan_fractional_count": ("if (local) ns++; else nf++;",
+                                    "if (local) ns++; else nf++;\n        if (l == L - 1) "
+                                    "ns = L * a / (a + b), nf = L - ns;"),
     "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
                           "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
 }
