@@ -44,7 +44,7 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 # Symbols declared in include/swa.h (checked by the CPU tests).
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
            "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
-           "swa_fwd_varlen", "swa_last_error")
+           "swa_fwd_varlen", "swa_layer_plan", "swa_cache_bytes", "swa_last_error")
 
 
 class SwaError(RuntimeError):
@@ -88,10 +88,13 @@ def lib():
             L.swa_decode_workspace_size.restype = ctypes.c_size_t
             L.swa_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, F, P]
+            L.swa_layer_plan.argtypes = [I, I, I, I, P, P, P]
+            L.swa_cache_bytes.argtypes = [I, I, I, I, ctypes.c_int64, I, P, P]
             L.swa_last_error.argtypes = []
             L.swa_last_error.restype = ctypes.c_char_p
             for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
-                      "swa_prefill_chunk", "swa_decode", "swa_bwd", "swa_fwd_varlen"):
+                      "swa_prefill_chunk", "swa_decode", "swa_bwd", "swa_fwd_varlen",
+                      "swa_layer_plan", "swa_cache_bytes"):
                 getattr(L, n).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -150,6 +153,37 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
            "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink, "max_len": nq}
     out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
     return out
+
+
+def swa_layer_plan(L, ratio, W):
+    """Per-layer windows of an L-layer stack for a local:global ratio given as
+    "a:b" or (a, b).  Returns (W_layer int32 [L] with -1 for global layers,
+    L_s, L_f)."""
+    if isinstance(ratio, str):
+        parts = ratio.split(":")
+        if len(parts) != 2:
+            raise ValueError("ratio must look like 'a:b', got %r" % (ratio,))
+        ratio = parts
+    a, b = (int(x) for x in ratio)
+    w = np.zeros(max(1, L), dtype=np.int32)
+    ns, nf = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().swa_layer_plan(L, a, b, W, _hp(w), ctypes.byref(ns), ctypes.byref(nf)))
+    return w[:L].copy(), ns.value, nf.value
+
+
+def swa_cache_bytes(B, G, d, elem_bytes, T, W_layer):
+    """Bytes of the persistent K/V caches of a stack with windows W_layer
+    (-1 = global) after T tokens."""
+    w = _np_i32(W_layer)
+    if w is None or w.size == 0:
+        w = np.zeros(1, dtype=np.int32)
+        L = 0
+    else:
+        L = int(w.size)
+    out = ctypes.c_int64(0)
+    _check(lib().swa_cache_bytes(B, G, d, elem_bytes, ctypes.c_int64(T), L, _hp(w),
+                                 ctypes.byref(out)))
+    return int(out.value)
 
 
 def meta_to_device(meta, device):

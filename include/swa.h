@@ -236,6 +236,36 @@ int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
                int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
                void *o, void *workspace, size_t ws_bytes, float scale, void *stream);
 
+/* Which layers of a stack use the window ("LLMs from scratch, chapter 10:
+ * SWA and DSA", §10.2: a local:global ratio has to be resolved into whole
+ * layers; a stride option picks the windowed layers).  Host only.
+ * The stack repeats a period of n_local windowed layers followed by n_global
+ * global (full-history) layers, from layer 0 upward; L layers take the first
+ * L of that pattern (e.g. 26 layers at 5:1 give 22 windowed and 4 global).
+ * Writes W_layer[l] = W for a windowed layer and -1 for a global one (the
+ * (-1, -1) window of "Dense attention vs sliding-window sparse attention",
+ * §3.3, meaning dense), and the counts *L_s (windowed), *L_f (global).
+ * A windowed layer runs swa_fwd / swa_decode with W; a global layer is the
+ * same call with W >= the sequence length (dense causal).
+ * Errors: SWA_EINVAL for L < 0, a negative ratio part or 0:0, W < 1, NULL
+ * outputs (W_layer may be NULL only when L == 0). */
+int swa_layer_plan(int L, int n_local, int n_global, int W, int32_t *W_layer,
+                   int32_t *L_s, int32_t *L_f);
+
+/* Bytes of the persistent K and V caches of a layer stack after T tokens
+ * ("LLMs from scratch, chapter 10", §10.2): a layer with window W_layer[l]
+ * keeps min(T, W_layer[l]) rows per KV head, a global layer (-1) keeps T, so
+ *   *bytes = 2 * B * G * d * elem_bytes * sum_l kept_l
+ * which is the chapter's 2BGds[L_s min(T,W) + L_f T] when every windowed
+ * layer has the same W, and 2BWGds per windowed layer once T >= W (the ring
+ * cache swa_decode reads).  B requests, G KV heads of width d, elem_bytes
+ * bytes per element (2 for bf16).  Host only.
+ * Errors: SWA_EINVAL for B, G, d or elem_bytes < 1, T < 0, L < 0, a window
+ * that is neither >= 1 nor -1, a result beyond int64, NULL pointers
+ * (W_layer may be NULL only when L == 0). */
+int swa_cache_bytes(int B, int G, int d, int elem_bytes, int64_t T, int L,
+                    const int32_t *W_layer, int64_t *bytes);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *swa_last_error(void);
 
