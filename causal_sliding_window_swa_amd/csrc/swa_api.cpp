@@ -63,6 +63,15 @@ int check_dtype_d(const char *fn, swa_dtype dt, int d) {
     return SWA_OK;
 }
 
+// The bf16 tile kernels address one (request, KV head) run of K/V rows with
+// 32-bit buffer offsets: `rows` rows `row_bytes` apart must span < 2^31 bytes.
+int check_span(const char *fn, swa_dtype dt, long long rows, long long row_bytes) {
+    if (dt == SWA_BF16 && rows * row_bytes > (long long)INT_MAX)
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 K/V rows of one head span %lld bytes (limit 2^31)",
+                    fn, rows * row_bytes);
+    return SWA_OK;
+}
+
 int check_tiles(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
     if (tile_q < 1 || tile_k < 1)
         return fail(SWA_EINVAL, "%s: tiles must be >= 1 (%d, %d)", fn, tile_q, tile_k);
@@ -95,6 +104,7 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
     if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_span(fn, dt, N, 2LL * d))) return rc;
     const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
     if ((rc = check_ptrs(fn, ptrs, names, 6))) return rc;
@@ -133,6 +143,7 @@ extern "C" int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
     if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
     if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_span(fn, dt, max_len, 2LL * d * Hkv))) return rc;
     const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
     if ((rc = check_ptrs(fn, ptrs, names, 6))) return rc;
@@ -218,6 +229,7 @@ extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, in
     if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
     if (W % tile_k != 0)
         return fail(SWA_EINVAL, "%s: W=%d must be a multiple of tile_k=%d", fn, W, tile_k);
+    if ((rc = check_span(fn, dt, W, 2LL * d))) return rc;
     const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o", "row_ptr", "col"};
     if ((rc = check_ptrs(fn, ptrs, names, 8))) return rc;

@@ -16,10 +16,15 @@
 //     XCD's L2;
 //   * wave priority is raised over the MFMA sections, so that while one wave
 //     issues its matrix work the co-resident wave fills the VALU slots;
-//   * K and V tiles go straight from HBM to LDS (global_load_lds_dwordx4, no
-//     register staging), double-buffered: the next tile streams in while this
-//     one is computed; rows are XOR-swizzled in 16-byte chunks so that both
-//     LDS read patterns below are free of bank conflicts;
+//   * K and V tiles go straight from HBM to LDS (buffer_load_dwordx4 ... lds,
+//     no register staging), double-buffered: the next tile streams in while
+//     this one is computed; rows are XOR-swizzled in 16-byte chunks so that
+//     both LDS read patterns below are free of bank conflicts.  The buffer
+//     (MUBUF) form of the LDS DMA matters: with the FLAT-encoded
+//     global_load_lds in flight the compiler can only wait for all LDS reads
+//     at once (lgkmcnt(0)); with it, K fragments are read ahead with partial
+//     waits.  The buffer range check returns zeros for rows past the data, so
+//     the ragged last tile needs no clamping;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows read from LDS,
 //     B = the wave's 32 query rows kept in registers.  Each lane then holds
 //     one query column, so row max and sum need one swap across wave halves;
@@ -169,37 +174,31 @@ void tile_kernel(AttnArgs a) {
         koff[i] = (uint32_t)(r * RSB + (pch ^ kswz(r)) * 16);
         voff[i] = (uint32_t)(r * RSB + (pch ^ vswz(r)) * 16);
     }
+    // buffer resources of the linear K/V rows (and the ring): loads past the
+    // last row return zeros (raw buffer range check), so the ragged last tile
+    // needs no clamping
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int lin_bytes = nrows > 0 ? (nrows - 1) * RSB + ROWB : 0;
+    const __amdgpu_buffer_rsrc_t klr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)klin, 0, lin_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vlr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)vlin, 0, lin_bytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t krr = klr, vrr = vlr;
+    if (MODE == 1) {
+        krr = __builtin_amdgcn_make_buffer_rsrc((void *)kring, 0, a.W * ROWB, 0x00020000);
+        vrr = __builtin_amdgcn_make_buffer_rsrc((void *)vring, 0, a.W * ROWB, 0x00020000);
+    }
     auto issue = [&](int kt, char *kdst) {
         char *vdst = kdst + TILEB;
         const bool ring = (MODE == 1) && kt < kp.nrt;
-        const int t0 = ring ? kt * BN : (kt - kp.nrt) * BN;  // first row of the tile
-        const char *kb = ring ? (const char *)(kring + (size_t)t0 * D)
-                              : (const char *)klin + (size_t)t0 * RSB;
-        const char *vb = ring ? (const char *)(vring + (size_t)t0 * D)
-                              : (const char *)vlin + (size_t)t0 * RSB;
-        if (ring || t0 + BN <= nrows) {
+        const int base = ring ? kt * BN * ROWB : (kt - kp.nrt) * BN * RSB;
 #pragma unroll
-            for (int i = 0; i < LPW; i++) {
-                const int ins = wave * LPW + i;
-                __builtin_amdgcn_global_load_lds((const void *)(kb + koff[i]),
-                                                 (void *)(kdst + ins * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vb + voff[i]),
-                                                 (void *)(vdst + ins * 1024), 16, 0, 0);
-            }
-        } else {  // ragged last tile: rows past the data are clamped to the last row
-#pragma unroll
-            for (int i = 0; i < LPW; i++) {
-                const int ins = wave * LPW + i;
-                const int r = ins * RPL + lane / CPR;
-                const int rc = (t0 + r < nrows) ? r : nrows - 1 - t0;  // 0 <= rc < nrows - t0
-                // same chunk, row rc: a non-negative offset inside the data
-                const int ko = (int)koff[i] + (rc - r) * RSB;
-                const int vo = (int)voff[i] + (rc - r) * RSB;
-                __builtin_amdgcn_global_load_lds((const void *)(kb + ko),
-                                                 (void *)(kdst + ins * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vb + vo),
-                                                 (void *)(vdst + ins * 1024), 16, 0, 0);
-            }
+        for (int i = 0; i < LPW; i++) {
+            const int ins = wave * LPW + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? krr : klr, (lds_void *)(kdst + ins * 1024),
+                                                     16, base + (int)koff[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? vrr : vlr, (lds_void *)(vdst + ins * 1024),
+                                                     16, base + (int)voff[i], 0, 0, 0);
         }
     };
 
@@ -305,11 +304,26 @@ void tile_kernel(AttnArgs a) {
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
             };
             if (live[0] && live[1]) {
+                // all K fragments of key block 0 first, then its MFMAs while the
+                // fragments of block 1 stream in behind them
+                bf16x8 kf[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
-                    qk_step(0, ks);
-                    qk_step(1, ks);
+                    const int c = (2 * ks + hh) ^ kswz(kr_row);
+                    kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + kr_row * ROWB + c * 16));
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
+                    const int r = 32 + kr_row;
+                    const int c = (2 * ks + hh) ^ kswz(r);
+                    kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++)
+                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[1], 0, 0, 0);
             } else if (live[0]) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(0, ks);

@@ -121,7 +121,8 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q
  * are read, and only partial ones are masked per element.  The kernel does
  * not re-check the metadata: metadata of other shapes is a caller error.
  * Supported: SWA_BF16 with d in {64, 128}, (tile_q, tile_k) = (128, 64) or
- * (64, 64); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
+ * (64, 64), and N * d * 2 < 2^31 (one head's K rows are addressed with 32-bit
+ * offsets); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
  * W >= N is legal (dense causal).
  * lse_dev: NULL, or device fp32 [B][H][N] that receives each row's natural-log
  * log-sum-exp of its visible scaled scores (-inf for rows that see no key),
@@ -146,8 +147,9 @@ int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
  * q_len = k_len = the lengths (host copy), the call's W, n_sink and tiles.
  * No padding is read or written.  The kernel does not re-check cu_seqlens
  * against the metadata: inconsistent ones are a caller error.
- * Supported and errors: as swa_fwd (max_len in place of N), plus SWA_EINVAL
- * for total < 1, max_len outside [1, total] or NULL cu_seqlens_dev. */
+ * Supported and errors: as swa_fwd (max_len * Hkv * d * 2 < 2^31 in place of
+ * N * d * 2 for bf16), plus SWA_EINVAL for total < 1, max_len outside
+ * [1, total] or NULL cu_seqlens_dev. */
 int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len, int d, int W,
                    int n_sink, int tile_q, int tile_k,
                    const void *q, const void *k, const void *v, void *o,
@@ -197,7 +199,8 @@ int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
  * cache_len = min(W, cache_len + Tq), ring_start = slot of the oldest kept
  * position.  Metadata: swa_blockmask_build with W_ring = W, nq = nk_lin = Tq,
  * q_start = k_start = next_pos and the same tiles.
- * Supported: as swa_fwd, plus W % tile_k == 0 and 1 <= Tq <= W.
+ * Supported: as swa_fwd (W * d * 2 < 2^31 for bf16), plus W % tile_k == 0
+ * and 1 <= Tq <= W.
  * Errors: as swa_fwd. */
 int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
                       int tile_q, int tile_k,

@@ -148,3 +148,22 @@ def test_decode_validation_codes():
     assert _decode(sink=4, sink_ptr=0) == swa.SWA_EINVAL  # sink caches required
     assert _decode(sink=4, sink_ptr=8) == swa.SWA_EINVAL  # misaligned
     assert swa.swa_decode_workspace_size(0, 32, 128, 4096) == 0
+
+
+def test_bf16_span_limit():
+    """The bf16 tile kernels address one head's K/V rows with 32-bit offsets:
+    longer spans are refused before any launch (no device memory needed)."""
+    L = swa.lib()
+    P = ctypes.c_void_p(16)
+    # N * d * 2 = 2^31 for N = 2^23, d = 128
+    rc = L.swa_fwd(0, 1, 1, 1, 1 << 23, 128, 64, 0, 128, 64, P, P, P, P, None, P, P, P, None,
+                   ctypes.c_float(0.1), None)
+    assert rc == 2 and b"span" in L.swa_last_error()
+    # varlen: max_len * Hkv * d * 2 = 2^31 for max_len = 2^20, Hkv = 8
+    rc = L.swa_fwd_varlen(0, 1, 8, 8, 1 << 20, 1 << 20, 128, 64, 0, 128, 64, P, P, P, P, P, P, P,
+                          P, None, ctypes.c_float(0.1), None)
+    assert rc == 2 and b"span" in L.swa_last_error()
+    # fp32 has no such limit at this check (it reaches other validation instead)
+    rc = L.swa_fwd(1, 1, 1, 1, 1 << 23, 128, 64, 0, 128, 64, P, P, P, P, None, P, P, P, None,
+                   ctypes.c_float(0.1), None)
+    assert b"span" not in L.swa_last_error()
