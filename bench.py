@@ -7,10 +7,12 @@ Prints ONE JSON line.  The headline step is the full-sequence SWA forward on
 the prefill workload (B=1, H=Hkv=32, N=8192, W=512, d=128, bf16, tiles
 128x64), whose block metadata is built once on the host beforehand (a fixed
 pattern reuses its metadata); `value` is useful TFLOP/s = 4*d*(visible pairs)
-per step over the wall time of K steps.  The same run also measures, each on
-its own synthetic workload, the GQA prefill with per-sequence lengths, the
-chunked prefill against a ring cache and the ring decode (KV GB/s), and times
-the fp64 oracle on a bounded sample on the host cores.
+per step over the wall time of K steps, replayed from a HIP graph that holds
+them (the eager per-step wall time is reported beside it).  The same run also
+measures, each on its own synthetic workload, the GQA prefill with
+per-sequence lengths, the chunked prefill against a ring cache and the ring
+decode (KV GB/s), and times the fp64 oracle on a bounded sample on the host
+cores.
 Inputs are seeded synthetic tensors already resident in HBM.
 """
 from __future__ import annotations
@@ -94,8 +96,12 @@ def main():
     K, WU = args.steps, args.warmup
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
-    def timed(fn, steps, warmup, reset=None):
-        """wall ms per step over `steps` launches, and mean event-timed ms."""
+    def timed(fn, steps, warmup, reset=None, graph=True):
+        """(ms per step, mean event-timed ms per step, eager wall ms per step).
+        The first figure is the wall time of one replay of a HIP graph holding
+        the `steps` steps (captured once, after the eager runs), so that the
+        host's per-launch cost between steps is not counted; with graph=False
+        (steps with host work) it is the eager wall time."""
         for _ in range(warmup):
             if reset:
                 reset()
@@ -118,7 +124,22 @@ def main():
             e.record(stream)
         torch.cuda.synchronize()
         ev = sum(s.elapsed_time(e) for s, e in evs) / steps
-        return wall, ev
+        if not graph:
+            return wall, ev, wall
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                if reset:
+                    reset()
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / steps
+        del g
+        return gms, ev, wall
 
     out = {}
 
@@ -139,16 +160,17 @@ def main():
     o = torch.empty_like(q)
     flops = 4.0 * d * meta["valid_pairs"] * H
     fwd = lambda: swa.swa_fwd(q, k, v, o, W, md)
-    wall_ms, ev_ms = timed(fwd, K, WU)
-    log("prefill: wall %.4f ms/step, event %.4f ms/launch" % (wall_ms, ev_ms))
+    wall_ms, ev_ms, eager_ms = timed(fwd, K, WU)
+    log("prefill: graph %.4f ms/step, eager %.4f ms/step, event %.4f ms/launch" % (
+        wall_ms, eager_ms, ev_ms))
     # end to end with the metadata rebuilt and copied each step
     def fwd_with_meta():
         m = swa.swa_blockmask_build(B, N, N, W, tq, tk)
         mdd = swa.meta_to_device(m, dev)
         swa.swa_fwd(q, k, v, o, W, mdd)
-    e2e_ms, _ = timed(fwd_with_meta, max(5, K // 5), 2)
-    prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, flops=flops, meta_ms=t_meta,
-                   meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
+    e2e_ms, _, _ = timed(fwd_with_meta, max(5, K // 5), 2, graph=False)
+    prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, eager_ms=eager_ms, flops=flops,
+                   meta_ms=t_meta, meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
     out["prefill"] = prefill
 
     # ---------------- backward on the prefill workload -------------
@@ -161,7 +183,7 @@ def main():
         wsb = torch.empty(swa.swa_bwd_workspace_size(B, H, N) // 4, dtype=torch.float32,
                           device=dev)
         fb = lambda: swa.swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, wsb, W, md)
-        wb, eb = timed(fb, max(3, K // 10), 1)
+        wb, eb, _ = timed(fb, max(3, K // 10), 1)
         out["bwd"] = dict(wall_ms=wb, kernel_ms=eb, flops=2.5 * flops)
         log("bwd: wall %.3f ms, event %.3f ms" % (wb, eb))
         del dout, lse, dq, dk, dv, wsb
@@ -171,7 +193,7 @@ def main():
         ms = swa.swa_blockmask_build(B, N, N, W, tq, tk, n_sink=4)
         mds = swa.meta_to_device(ms, dev)
         fs = lambda: swa.swa_fwd(q, k, v, o, W, mds)
-        ws_, es_ = timed(fs, K, WU)
+        ws_, es_, _ = timed(fs, K, WU)
         out["prefill_sink"] = dict(wall_ms=ws_, kernel_ms=es_,
                                    flops=4.0 * d * ms["valid_pairs"] * H)
         log("prefill sink: wall %.4f ms, event %.4f ms" % (ws_, es_))
@@ -189,7 +211,7 @@ def main():
         o3 = torch.empty_like(q3)
         del inp
         f3 = lambda: swa.swa_fwd(q3, k3, v3, o3, 4096, md3, q_len=ql3)
-        w3, e3 = timed(f3, max(3, K // 10), 2)
+        w3, e3, _ = timed(f3, max(3, K // 10), 2)
         out["gqa"] = dict(wall_ms=w3, kernel_ms=e3, flops=4.0 * d3 * m3["valid_pairs"] * H3)
         log("gqa: wall %.3f ms, event %.3f ms" % (w3, e3))
         # the same sequences packed token-major without padding (swa_fwd_varlen)
@@ -200,7 +222,7 @@ def main():
         cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
         op = torch.empty_like(pk[0])
         f3p = lambda: swa.swa_fwd_varlen(pk[0], pk[1], pk[2], op, 4096, md3, cu)
-        w3p, e3p = timed(f3p, max(3, K // 10), 2)
+        w3p, e3p, _ = timed(f3p, max(3, K // 10), 2)
         out["gqa_packed"] = dict(wall_ms=w3p, kernel_ms=e3p, flops=out["gqa"]["flops"],
                                  tokens=int(sum(lens)))
         log("gqa packed: wall %.3f ms, event %.3f ms" % (w3p, e3p))
@@ -228,7 +250,7 @@ def main():
         f4 = lambda: swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
                                            dv["v_cache"], dv["ring_start"], dv["cache_len"],
                                            dv["next_pos"], o4, W4, md4)
-        w4, e4 = timed(f4, max(5, K // 5), 2, reset=reset4)
+        w4, e4, _ = timed(f4, max(5, K // 5), 2, reset=reset4)
         out["chunk"] = dict(wall_ms=w4, kernel_ms=e4, flops=4.0 * d4 * m4["valid_pairs"] * H4,
                             keys_touched_per_request=m4["keys_touched"] // B4)
         log("chunk: wall %.3f ms, event %.3f ms" % (w4, e4))
@@ -248,9 +270,9 @@ def main():
         f5 = lambda: swa.swa_decode(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
                                     dv["v_cache"], dv["ring_start"], dv["cache_len"],
                                     dv["next_pos"], o5, ws, W5)
-        w5, e5 = timed(f5, max(10, K), 5)
+        w5, e5, we5 = timed(f5, max(10, K), 5)
         kv_bytes = 2.0 * B5 * Hkv5 * W5 * d5 * 2
-        out["decode"] = dict(wall_ms=w5, kernel_ms=e5, kv_bytes=kv_bytes)
+        out["decode"] = dict(wall_ms=w5, kernel_ms=e5, eager_ms=we5, kv_bytes=kv_bytes)
         log("decode: wall %.4f ms, event %.4f ms" % (w5, e5))
         if "sink" in only:  # 4 sinks, all outside the window at these positions
             sk = torch.zeros(B5, Hkv5, 4, d5, dtype=dv["k_cache"].dtype, device=dev)
@@ -259,7 +281,7 @@ def main():
                                         dv["v_cache"], dv["ring_start"], dv["cache_len"],
                                         dv["next_pos"], o5, ws, W5, n_sink=4, sink_k=sk,
                                         sink_v=sv)
-            w6, e6 = timed(f6, max(10, K), 5)
+            w6, e6, _ = timed(f6, max(10, K), 5)
             out["decode_sink"] = dict(wall_ms=w6, kernel_ms=e6,
                                       kv_bytes=kv_bytes + 2.0 * B5 * Hkv5 * 4 * d5 * 2)
             log("decode sink: wall %.4f ms, event %.4f ms" % (w6, e6))
@@ -301,6 +323,7 @@ def main():
         "steps": K,
         "warmup": WU,
         "ms_per_step": round(pf["wall_ms"], 5),
+        "eager_ms_per_step": round(pf["eager_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -331,8 +354,10 @@ def main():
         gbs = dd["kv_bytes"] / (dd["wall_ms"] * 1e-3) / 1e9
         gbs_k = dd["kv_bytes"] / (dd["kernel_ms"] * 1e-3) / 1e9
         line["decode"] = {"workload": "decode B=64 H=32 Hkv=8 W=4096 d=128 bf16, full rings",
-                          "GB_per_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                          "GB_per_s": round(gbs, 1),
+                          "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                           "ms_per_step": round(dd["wall_ms"], 5),
+                          "eager_ms_per_step": round(dd["eager_ms"], 5),
                           "roofline": {"bound": "hbm", "achieved": round(gbs_k, 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": round(gbs_k / PEAK_HBM_GBS, 4),

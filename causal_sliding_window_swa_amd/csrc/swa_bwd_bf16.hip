@@ -84,21 +84,42 @@ __device__ __forceinline__ bf16x8 row_frag(const char *base, int r0, int lq, int
     return __builtin_bit_cast(bf16x8, *(const u32x4 *)(base + r * ROWB + c * 16));
 }
 
-// Copy 64 rows x D of a row-major bf16 matrix (rows row0.., clamped to
-// rows < nrows) into an LDS tile, swizzled; NW waves share the work.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at `base`: raw loads past the end return 0.
+#define SWA_RSRC(base, bytes) \
+    __builtin_amdgcn_make_buffer_rsrc((void *)(base), 0, (bytes), 0x00020000)
+
+// Copy 64 rows x D of a row-major bf16 matrix of nrows rows (rows row0..;
+// rows past the data read as zeros: finite, and masked) into an LDS tile,
+// swizzled; NW waves share the work.  The buffer (MUBUF) form of the LDS DMA
+// keeps the compiler's LDS-read waits partial (the FLAT global_load_lds form
+// makes every wait lgkmcnt(0)).
 template <int D, int NW>
 __device__ __forceinline__ void stage_rows(const __bf16 *src, int row0, int nrows, char *dst,
                                            int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist for the device only
     constexpr int ROWB = D * 2, CPR = D / 8, RPL = 64 / CPR, LPW = BN / RPL / NW;
+    const auto rs = SWA_RSRC(src, nrows * ROWB);
 #pragma unroll
     for (int i = 0; i < LPW; i++) {
         const int ins = wave * LPW + i;
         const int r = ins * RPL + lane / CPR;
         const int pch = lane % CPR;
-        const int rr = min(row0 + r, nrows - 1);  // rows past the data: a real row, masked
-        const char *s = (const char *)(src + (size_t)rr * D) + (pch ^ swz<CPR>(r)) * 16;
-        __builtin_amdgcn_global_load_lds((const void *)s, (void *)(dst + ins * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + ins * 1024), 16,
+                                                 (row0 + r) * ROWB + (pch ^ swz<CPR>(r)) * 16, 0,
+                                                 0, 0);
     }
+#endif
+}
+
+// One fp32 value per lane (index i of an n-element array; zero past the end)
+// into 64 consecutive LDS words.
+__device__ __forceinline__ void stage_vals(const float *src, int i, int n, char *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(SWA_RSRC(src, n * 4), (lds_void *)dst, 4, i * 4, 0,
+                                             0, 0);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -342,10 +363,9 @@ void dkdv_kernel(BwdArgs a) {
         const size_t rb = ((size_t)b * a.H + hq) * N;
         stage_rows<D, NW>((const __bf16 *)a.q + rb * D, s0, N, dst, wave, lane);
         stage_rows<D, NW>((const __bf16 *)a.dout + rb * D, s0, N, dst + TILEB, wave, lane);
-        const int rr = min(s0 + lane, N - 1);
-        const float *src = (wave == 0) ? (a.lse + rb + rr) : (a.dvec + rb + rr);
-        __builtin_amdgcn_global_load_lds((const void *)src, (void *)(dst + 2 * TILEB + wave * 256),
-                                         4, 0, 0);
+        // row values of the 64 rows (zeros past the data, which is masked)
+        const float *src = (wave == 0) ? (a.lse + rb) : (a.dvec + rb);
+        stage_vals(src, s0 + lane, N, dst + 2 * TILEB + wave * 256);
     };
 
     const int tr_j = lane & 15;

@@ -195,10 +195,12 @@ void tile_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < LPW; i++) {
             const int ins = wave * LPW + i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? krr : klr, (lds_void *)(kdst + ins * 1024),
-                                                     16, base + (int)koff[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? vrr : vlr, (lds_void *)(vdst + ins * 1024),
-                                                     16, base + (int)voff[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? krr : klr,
+                                                     (lds_void *)(kdst + ins * 1024), 16,
+                                                     base + (int)koff[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? vrr : vlr,
+                                                     (lds_void *)(vdst + ins * 1024), 16,
+                                                     base + (int)voff[i], 0, 0, 0);
         }
     };
 
@@ -310,20 +312,22 @@ void tile_kernel(AttnArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
                     const int c = (2 * ks + hh) ^ kswz(kr_row);
-                    kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + kr_row * ROWB + c * 16));
+                    kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksm + kr_row * ROWB + c * 16));
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
-                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
+                    sacc[0] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
                     const int r = 32 + kr_row;
                     const int c = (2 * ks + hh) ^ kswz(r);
-                    kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
+                    kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksm + r * ROWB + c * 16));
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++)
-                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[1], 0, 0, 0);
+                    sacc[1] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[1], 0, 0, 0);
             } else if (live[0]) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(0, ks);
