@@ -68,6 +68,8 @@ class Oracle:
         lib.orc_fwd_rows_sink.restype = None
         lib.orc_chunk.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, P, d, P]
         lib.orc_chunk.restype = None
+        lib.orc_chunk_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, d, P]
+        lib.orc_chunk_sink.restype = None
         lib.orc_decode_sink.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, d, P]
         lib.orc_decode_sink.restype = None
         lib.orc_blockmask_sink.argtypes = [i, i, i, i, i, i, i, P, P, P, P, i, P, P, P,
@@ -187,15 +189,22 @@ class Oracle:
         return dq, dk, dv
 
     def chunk(self, q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos,
-              W: int, scale: float):
+              W: int, scale: float, n_sink: int = 0, sink_k=None, sink_v=None):
         """Chunked prefill against a ring cache.  Returns (o, k_cache', v_cache',
-        ring_start', cache_len', next_pos'); the inputs are not modified."""
+        ring_start', cache_len', next_pos'); with n_sink > 0 also sink_k', sink_v'
+        ([B,Hkv,n_sink,d] sink caches).  The inputs are not modified."""
         q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
         kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
         rs, cl, npos = (_i32(x).copy() for x in (ring_start, cache_len, next_pos))
         B, H, Tq, dd = q.shape
         Hkv = kn.shape[1]
         o = np.empty_like(q)
+        if n_sink > 0:
+            sk, sv = _f64(sink_k).copy(), _f64(sink_v).copy()
+            self.lib.orc_chunk_sink(B, H, Hkv, Tq, dd, W, n_sink, _ptr(q), _ptr(kn), _ptr(vn),
+                                    _ptr(kc), _ptr(vc), _ptr(sk), _ptr(sv), _ptr(rs), _ptr(cl),
+                                    _ptr(npos), float(scale), _ptr(o))
+            return o, kc, vc, rs, cl, npos, sk, sv
         self.lib.orc_chunk(B, H, Hkv, Tq, dd, W, _ptr(q), _ptr(kn), _ptr(vn), _ptr(kc),
                            _ptr(vc), _ptr(rs), _ptr(cl), _ptr(npos), float(scale), _ptr(o))
         return o, kc, vc, rs, cl, npos

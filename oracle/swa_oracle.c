@@ -247,48 +247,61 @@ static void ring_append_one(int Hkv, int W, int d, double *kc, double *vc,
  * next_pos.  Every query attends over that union (which is why the step
  * needs up to W+Tq-1 keys although only W stay cached).  Afterwards the new
  * rows are appended to the ring one by one, so the ring keeps the last W.
+ * With S > 0 sink tokens ("Sparse attention taxonomy" §3.2) the sink cache
+ * sink_k, sink_v [B][Hkv][S][d] holds the rows of positions 0 .. S-1
+ * (READING, as in decode): the queries also attend over the sink positions
+ * that neither the ring nor the chunk holds (each position once), and new
+ * tokens at positions below S are copied into the sink cache at commit.
  * q: [B][H][Tq][d]; k_new, v_new: [B][Hkv][Tq][d];
  * k_cache, v_cache: [B][Hkv][W][d] (in/out); ring state arrays [B] (in/out);
  * o: [B][H][Tq][d]. */
-void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
-               const double *q, const double *k_new, const double *v_new,
-               double *k_cache, double *v_cache,
-               int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
-               double scale, double *o)
+void orc_chunk_sink(int B, int H, int Hkv, int Tq, int d, int W, int S,
+                    const double *q, const double *k_new, const double *v_new,
+                    double *k_cache, double *v_cache, double *sink_k, double *sink_v,
+                    int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+                    double scale, double *o)
 {
     int b;
     const int G = H / Hkv;
     for (b = 0; b < B; b++) {
         const int old_len = cache_len[b];
         const int64_t p0 = next_pos[b];
-        const int nk = old_len + Tq;
-        int h, t;
+        const int64_t oldest = p0 - old_len; /* oldest position the ring holds */
+        const int nsink = (int)(S < oldest ? S : (oldest > 0 ? oldest : 0));
+        const int nk = nsink + old_len + Tq;
+        int h, t, g;
         for (h = 0; h < H; h++) {
-            const int64_t g = h / G;
-            const double *kc = k_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
-            const double *vc = v_cache + ((int64_t)b * Hkv + g) * (int64_t)W * d;
-            const double *kn = k_new + ((int64_t)b * Hkv + g) * (int64_t)Tq * d;
-            const double *vn = v_new + ((int64_t)b * Hkv + g) * (int64_t)Tq * d;
+            const int64_t gg = h / G;
+            const double *kc = k_cache + ((int64_t)b * Hkv + gg) * (int64_t)W * d;
+            const double *vc = v_cache + ((int64_t)b * Hkv + gg) * (int64_t)W * d;
+            const double *kn = k_new + ((int64_t)b * Hkv + gg) * (int64_t)Tq * d;
+            const double *vn = v_new + ((int64_t)b * Hkv + gg) * (int64_t)Tq * d;
             const double **kr = malloc(sizeof(*kr) * (size_t)nk);
             const double **vr = malloc(sizeof(*vr) * (size_t)nk);
             int64_t *kp = malloc(sizeof(*kp) * (size_t)nk);
             int r;
+            /* sink positions held by neither the ring nor the chunk */
+            for (r = 0; r < nsink; r++) {
+                kr[r] = sink_k + (((int64_t)b * Hkv + gg) * S + r) * d;
+                vr[r] = sink_v + (((int64_t)b * Hkv + gg) * S + r) * d;
+                kp[r] = r;
+            }
             /* combined keys: old cache in logical order, then the new rows */
             for (r = 0; r < old_len; r++) {
                 const int slot = (ring_start[b] + r) % W;
-                kr[r] = kc + (int64_t)slot * d;
-                vr[r] = vc + (int64_t)slot * d;
-                kp[r] = p0 - old_len + r; /* k_start_pos_abs = ptr - old_len */
+                kr[nsink + r] = kc + (int64_t)slot * d;
+                vr[nsink + r] = vc + (int64_t)slot * d;
+                kp[nsink + r] = p0 - old_len + r; /* k_start_pos_abs = ptr - old_len */
             }
             for (t = 0; t < Tq; t++) {
-                kr[old_len + t] = kn + (int64_t)t * d;
-                vr[old_len + t] = vn + (int64_t)t * d;
-                kp[old_len + t] = p0 + t;
+                kr[nsink + old_len + t] = kn + (int64_t)t * d;
+                vr[nsink + old_len + t] = vn + (int64_t)t * d;
+                kp[nsink + old_len + t] = p0 + t;
             }
 #pragma omp parallel for schedule(dynamic, 4)
             for (t = 0; t < Tq; t++) {
                 double *sc = malloc(sizeof(*sc) * (size_t)nk);
-                attend_row(d, W, 0, scale,
+                attend_row(d, W, S, scale,
                            q + (((int64_t)b * H + h) * Tq + t) * d, p0 + t,
                            nk, kr, vr, kp, sc,
                            o + (((int64_t)b * H + h) * Tq + t) * d);
@@ -297,7 +310,16 @@ void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
             free(kr); free(vr); free(kp);
         }
         /* commit only after every query of the chunk has read the old ring */
-        for (t = 0; t < Tq; t++)
+        for (t = 0; t < Tq; t++) {
+            if (p0 + t < S) {
+                for (g = 0; g < Hkv; g++) {
+                    const int64_t slot = ((int64_t)b * Hkv + g) * S + p0 + t;
+                    memcpy(sink_k + slot * d, k_new + (((int64_t)b * Hkv + g) * Tq + t) * d,
+                           sizeof(double) * (size_t)d);
+                    memcpy(sink_v + slot * d, v_new + (((int64_t)b * Hkv + g) * Tq + t) * d,
+                           sizeof(double) * (size_t)d);
+                }
+            }
             ring_append_one(Hkv, W, d,
                             k_cache + (int64_t)b * Hkv * W * d,
                             v_cache + (int64_t)b * Hkv * W * d,
@@ -305,7 +327,18 @@ void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
                             k_new + ((int64_t)b * Hkv * Tq + t) * d,
                             v_new + ((int64_t)b * Hkv * Tq + t) * d,
                             (int64_t)Tq * d);
+        }
     }
+}
+
+void orc_chunk(int B, int H, int Hkv, int Tq, int d, int W,
+               const double *q, const double *k_new, const double *v_new,
+               double *k_cache, double *v_cache,
+               int32_t *ring_start, int32_t *cache_len, int32_t *next_pos,
+               double scale, double *o)
+{
+    orc_chunk_sink(B, H, Hkv, Tq, d, W, 0, q, k_new, v_new, k_cache, v_cache, NULL, NULL,
+                   ring_start, cache_len, next_pos, scale, o);
 }
 
 /* One decode step: the new token's K/V row is appended to the ring first

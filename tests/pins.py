@@ -687,6 +687,37 @@ def pin_sink_decode_streams_like_full(O):
     assert np.array_equal(sk, k[:, :, :S].transpose(0, 1, 2, 3))
 
 
+def pin_sink_chunk_streams_like_full(O):
+    """Chunked prefill with sinks, chunks of several sizes mixed with decode
+    steps from an empty ring, reproduces the full-sequence sink forward row by
+    row; the sink cache ends up holding exactly the first S positions."""
+    rng = _rng(62)
+    B, H, Hkv, T, d, W, S = 2, 4, 2, 29, 6, 5, 3
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    full = O.fwd(q, k, v, W=W, scale=0.5, n_sink=S)
+    kc = np.zeros((B, Hkv, W, d))
+    vc = np.zeros((B, Hkv, W, d))
+    sk = np.zeros((B, Hkv, S, d))
+    sv = np.zeros((B, Hkv, S, d))
+    rs, cl, npos = np.array([0, 4]), np.array([0, 0]), np.array([0, 0])
+    t = 0
+    for n in [2, 1, 4, 1, 5, 3, 1, 1, 5, 2, 4]:  # 1 = a decode step
+        if n == 1:
+            out = O.decode(q[:, :, t], k[:, :, t], v[:, :, t], kc, vc, rs, cl, npos, W=W,
+                           scale=0.5, n_sink=S, sink_k=sk, sink_v=sv)
+        else:
+            out = O.chunk(q[:, :, t:t + n], k[:, :, t:t + n], v[:, :, t:t + n], kc, vc, rs, cl,
+                          npos, W=W, scale=0.5, n_sink=S, sink_k=sk, sink_v=sv)
+        o, kc, vc, rs, cl, npos, sk, sv = out
+        ref = full[:, :, t] if n == 1 else full[:, :, t:t + n]
+        assert np.max(np.abs(o - ref)) <= 1e-12, (t, n)
+        t += n
+    assert t == T
+    assert np.array_equal(sk, k[:, :, :S]) and np.array_equal(sv, v[:, :, :S])
+
+
 def pin_sink_bwd(O):
     """Gradients with sinks: central differences of the sink forward, and torch
     autograd through SDPA with the library-built mask."""
@@ -853,6 +884,7 @@ PINS = [
     pin_sink_pair_counts_and_blocks,
     pin_sink_mask_sdpa,
     pin_sink_decode_streams_like_full,
+    pin_sink_chunk_streams_like_full,
     pin_sink_bwd,
     pin_varlen_equals_per_sequence,
     pin_cache_dense_example,

@@ -23,7 +23,8 @@ MUTANTS = {
     "gqa_interleaved": ("h / G", "h % Hkv"),
     "k_used_for_v": ("out[c] += e * vrow[j][c];", "out[c] += e * krow[j][c];"),
     "no_normalisation": ("out[c] /= l;", "out[c] /= 1.0;"),
-    "chunk_key_position_shift": ("kp[r] = p0 - old_len + r;", "kp[r] = p0 - old_len + r + 1;"),
+    "chunk_key_position_shift": ("kp[nsink + r] = p0 - old_len + r;",
+                                 "kp[nsink + r] = p0 - old_len + r + 1;"),
     "chunk_query_position_shift": ("p0 + t,\n", "p0 + t + 1,\n"),
     "ring_fill_ignores_start": ("slot = (*start + *len) % W;", "slot = *len % W;"),
     "ring_start_not_advanced": ("*start = (*start + 1) % W;", "*start = *start % W;"),
@@ -49,6 +50,9 @@ MUTANTS = {
     "sink_bound_off_by_one": ("(kpos < S && kpos <= qpos)", "(kpos <= S && kpos <= qpos)"),
     "sink_not_causal": ("(kpos < S && kpos <= qpos)", "(kpos < S)"),
     "sink_decode_double_count": ("nsink = (int)(S < oldest ? S : oldest);", "nsink = S;"),
+    "chunk_sink_cache_not_written": ("            if (p0 + t < S) {", "            if (p0 + t < 0) {"),
+    "chunk_sink_double_count": ("const int nsink = (int)(S < oldest ? S : (oldest > 0 ? oldest : 0));",
+                                "const int nsink = S;"),
     "sink_cache_not_written": ("if (S > 0 && next_pos[b] < S) {", "if (S > 0 && next_pos[b] < 0) {"),
     "varlen_key_from_previous_sequence": ("kr[j] = k + ((t0 + j) * Hkv + g) * d;",
                                           "kr[j] = k + ((t0 + j - (j == 0 && t0 > 0)) * Hkv + g) * d;"),
