@@ -235,8 +235,10 @@ class Oracle:
                   next_pos=None, n_sink=0):
         """Brute-force block metadata.  Returns a dict with cls [B,nqt,nkt] uint8,
         row_ptr [B*nqt+1] int32, col [nnz] int32, col_cls [nnz] uint8 and the six
-        statistics named in STAT_NAMES."""
-        nk = W_ring + nk_lin
+        statistics named in STAT_NAMES.  With a ring and n_sink > 0 the key axis
+        starts with n_sink rounded up to tile_k sink slots."""
+        ns = -(-n_sink // tile_k) * tile_k if (W_ring > 0 and n_sink > 0) else 0
+        nk = ns + W_ring + nk_lin
         nqt = -(-nq // tile_q)
         nkt = -(-nk // tile_k)
         cls = np.zeros((B, nqt, nkt), dtype=np.uint8)
@@ -248,10 +250,9 @@ class Oracle:
         qs, ks, ql, kl, rs, cl, npos = (_i32(x) for x in (
             q_start, k_start, q_len, k_len, ring_start, cache_len, next_pos))
         nnz = self.lib.orc_blockmask_sink(B, nq, nk_lin, W, n_sink, tile_q, tile_k, _ptr(qs),
-                                          _ptr(ks),
-                                     _ptr(ql), _ptr(kl), W_ring, _ptr(rs), _ptr(cl),
-                                     _ptr(npos), _ptr(cls), _ptr(row_ptr), _ptr(col),
-                                     _ptr(col_cls), _ptr(stats))
+                                          _ptr(ks), _ptr(ql), _ptr(kl), W_ring, _ptr(rs),
+                                          _ptr(cl), _ptr(npos), _ptr(cls), _ptr(row_ptr),
+                                          _ptr(col), _ptr(col_cls), _ptr(stats))
         out = {"cls": cls, "row_ptr": row_ptr, "col": col[:nnz].copy(),
                "col_cls": col_cls[:nnz].copy()}
         out.update({n: int(stats[i]) for i, n in enumerate(STAT_NAMES)})

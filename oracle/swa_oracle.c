@@ -435,6 +435,12 @@ void orc_decode(int B, int H, int Hkv, int d, int W,
  * k_start[b] + t and is valid iff t < k_len[b]; query i sits at q_start[b]+i
  * and is valid iff i < q_len[b].  NULL position arrays mean 0, NULL length
  * arrays mean "all valid".
+ * With a ring and S > 0 sinks (the chunk with sinks) the axis starts with a
+ * sink segment of NS = S rounded up to tile_k slots: slot s stands for
+ * position s (valid iff s < S) and is visible to every query at or after s;
+ * positions below S are then taken from that segment only, so ring and
+ * linear keys are visible by the window rule and only at positions >= S
+ * (READING: each position counted once, as the method's definition asks).
  *
  * Outputs: cls[b][qt][kt]; CSR over rows b*nqt+qt in ascending key tile
  * (row_ptr, col, col_cls); stats[6] = valid pairs, covered coordinates
@@ -448,7 +454,9 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
                            uint8_t *cls, int32_t *row_ptr, int32_t *col,
                            uint8_t *col_cls, int64_t *stats)
 {
-    const int nk = W_ring + nk_lin;
+    const int seg = W_ring > 0 && S > 0;
+    const int NS = seg ? (S + tile_k - 1) / tile_k * tile_k : 0;
+    const int nk = NS + W_ring + nk_lin;
     const int nqt = (nq + tile_q - 1) / tile_q;
     const int nkt = (nk + tile_k - 1) / tile_k;
     int64_t nnz = 0;
@@ -457,6 +465,7 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
     int64_t *kpos = malloc(sizeof(int64_t) * (size_t)(nk > 0 ? nk : 1));
     char *qok = malloc((size_t)(nq > 0 ? nq : 1));
     char *kok = malloc((size_t)(nk > 0 ? nk : 1));
+    char *ksink = malloc((size_t)(nk > 0 ? nk : 1));
     char *touched = malloc((size_t)(nk > 0 ? nk : 1));
     int64_t *counts = malloc(sizeof(int64_t) * (size_t)(nqt > 0 && nkt > 0 ? nqt * nkt : 1));
 
@@ -470,19 +479,26 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
             qpos[i] = (q_start ? q_start[b] : 0) + (int64_t)i;
             qok[i] = q_len ? (i < q_len[b]) : 1;
         }
+        for (j = 0; j < nk; j++)
+            ksink[j] = 0;
+        for (j = 0; j < NS; j++) {
+            kpos[j] = j;
+            kok[j] = j < S;
+            ksink[j] = 1;
+        }
         for (j = 0; j < W_ring; j++)
-            kok[j] = 0;
+            kok[NS + j] = 0;
         if (W_ring > 0) {
             int r;
             for (r = 0; r < cache_len[b]; r++) {
                 const int slot = (ring_start[b] + r) % W_ring;
-                kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r;
-                kok[slot] = 1;
+                kpos[NS + slot] = (int64_t)next_pos[b] - cache_len[b] + r;
+                kok[NS + slot] = 1;
             }
         }
         for (j = 0; j < nk_lin; j++) {
-            kpos[W_ring + j] = (k_start ? k_start[b] : 0) + (int64_t)j;
-            kok[W_ring + j] = k_len ? (j < k_len[b]) : 1;
+            kpos[NS + W_ring + j] = (k_start ? k_start[b] : 0) + (int64_t)j;
+            kok[NS + W_ring + j] = k_len ? (j < k_len[b]) : 1;
         }
         /* visible-pair count of every tile pair, by brute force over its
          * coordinates (tiles are independent: counted in parallel) */
@@ -497,7 +513,10 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
                 int ii, jj;
                 for (ii = i0; ii < i1; ii++)
                     for (jj = j0; jj < j1; jj++)
-                        if (qok[ii] && kok[jj] && visible(qpos[ii], kpos[jj], W, S))
+                        if (qok[ii] && kok[jj] &&
+                            (!seg ? visible(qpos[ii], kpos[jj], W, S)
+                                  : ksink[jj] ? kpos[jj] <= qpos[ii]
+                                              : visible(qpos[ii], kpos[jj], W, 0) && kpos[jj] >= S))
                             count++;
                 counts[(int64_t)qt * nkt + kt] = count;
             }
@@ -508,7 +527,10 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
             int ii;
             touched[j] = 0;
             for (ii = 0; ii < nq && kok[j]; ii++)
-                if (qok[ii] && visible(qpos[ii], kpos[j], W, S)) {
+                if (qok[ii] &&
+                    (!seg ? visible(qpos[ii], kpos[j], W, S)
+                          : ksink[j] ? kpos[j] <= qpos[ii]
+                                     : visible(qpos[ii], kpos[j], W, 0) && kpos[j] >= S)) {
                     touched[j] = 1;
                     break;
                 }
@@ -540,7 +562,7 @@ int64_t orc_blockmask_sink(int B, int nq, int nk_lin, int W, int S, int tile_q, 
         for (j = 0; j < nk; j++)
             stats[2] += touched[j];
     }
-    free(qpos); free(kpos); free(qok); free(kok); free(touched); free(counts);
+    free(qpos); free(kpos); free(qok); free(kok); free(ksink); free(touched); free(counts);
     return nnz;
 }
 

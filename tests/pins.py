@@ -647,6 +647,26 @@ def pin_sink_pair_counts_and_blocks(O):
     _check_aggregation(m, masks, 16, 8)
 
 
+def pin_sink_ring_metadata(O):
+    """Chunk metadata with sinks (sink segment before the ring): every query at
+    position t sees each position p <= t with p >= t-W+1 or p < S exactly once,
+    among the positions the sink segment, the ring and the chunk hold, so the
+    visible pairs are sum_t min(S, t+1) + max(0, t + 1 - max(S, t-W+1, oldest))
+    (oldest = first position the ring holds).  The sink slots come first and
+    are NS = S rounded up to tile_k."""
+    for W, S, Tq, tk, states in ((16, 4, 7, 8, [(3, 16, 40), (0, 5, 5), (9, 16, 18), (0, 0, 0)]),
+                                 (8, 3, 8, 4, [(2, 8, 30), (1, 4, 4), (5, 8, 9)])):
+        for rs, cl, p0 in states:
+            m = O.blockmask(1, Tq, Tq, W, 4, tk, q_start=[p0], k_start=[p0], W_ring=W,
+                            ring_start=[rs], cache_len=[cl], next_pos=[p0], n_sink=S)
+            oldest = p0 - cl
+            want = sum(min(S, t + 1) + max(0, t + 1 - max(S, t - W + 1, oldest))
+                       for t in range(p0, p0 + Tq))
+            assert m["valid_pairs"] == want, (W, S, rs, cl, p0, m["valid_pairs"], want)
+            ns = -(-S // tk) * tk
+            assert m["cls"].shape[2] == (ns + W + Tq + tk - 1) // tk
+
+
 def pin_sink_mask_sdpa(O):
     """Forward with sinks equals SDPA with the library-built mask; n_sink = 0
     gives the plain window exactly."""
@@ -882,6 +902,7 @@ PINS = [
     pin_bwd_selection_matches,
     pin_sink_visible_sets,
     pin_sink_pair_counts_and_blocks,
+    pin_sink_ring_metadata,
     pin_sink_mask_sdpa,
     pin_sink_decode_streams_like_full,
     pin_sink_chunk_streams_like_full,

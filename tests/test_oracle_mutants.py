@@ -53,6 +53,9 @@ MUTANTS = {
     "chunk_sink_cache_not_written": ("            if (p0 + t < S) {", "            if (p0 + t < 0) {"),
     "chunk_sink_double_count": ("const int nsink = (int)(S < oldest ? S : (oldest > 0 ? oldest : 0));",
                                 "const int nsink = S;"),
+    "ring_sink_counted_twice": (": visible(qpos[ii], kpos[jj], W, 0) && kpos[jj] >= S))",
+                                ": visible(qpos[ii], kpos[jj], W, 0) && kpos[jj] >= 0))"),
+    "sink_segment_ignores_causality": ("? kpos[jj] <= qpos[ii]", "? kpos[jj] >= 0"),
     "sink_cache_not_written": ("if (S > 0 && next_pos[b] < S) {", "if (S > 0 && next_pos[b] < 0) {"),
     "varlen_key_from_previous_sequence": ("kr[j] = k + ((t0 + j) * Hkv + g) * d;",
                                           "kr[j] = k + ((t0 + j - (j == 0 && t0 > 0)) * Hkv + g) * d;"),
