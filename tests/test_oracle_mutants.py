@@ -36,8 +36,8 @@ MUTANTS = {
     "full_threshold": ("(count == area ? 1 : 2)", "(count * 2 >= area ? 1 : 2)"),
     "edge_area_not_clipped": ("const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);",
                               "const int64_t area = (int64_t)tile_q * tile_k;"),
-    "ring_slot_position_shift": ("kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r;",
-                                 "kpos[slot] = (int64_t)next_pos[b] - cache_len[b] + r + 1;"),
+    "ring_slot_position_shift": ("kpos[NS + slot] = (int64_t)next_pos[b] - cache_len[b] + r;",
+                                 "kpos[NS + slot] = (int64_t)next_pos[b] - cache_len[b] + r + 1;"),
     "bwd_row_D_dropped": ("ds = p * (dp - D);", "ds = p * dp;"),
     "bwd_key_D_dropped": ("ds = p * (dp - Dv[row]);", "ds = p * dp;"),
     "bwd_dk_scale_dropped": ("dkj[c] += scale * ds * qi[c];", "dkj[c] += ds * qi[c];"),
