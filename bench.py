@@ -254,6 +254,22 @@ def main():
         out["chunk"] = dict(wall_ms=w4, kernel_ms=e4, flops=4.0 * d4 * m4["valid_pairs"] * H4,
                             keys_touched_per_request=m4["keys_touched"] // B4)
         log("chunk: wall %.3f ms, event %.3f ms" % (w4, e4))
+        if "sink" in only:  # 4 sinks from a sink cache, far behind every window
+            m4s = swa.swa_blockmask_build(B4, Tq, Tq, W4, tq, tk, q_start=p, k_start=p,
+                                          W_ring=W4, ring_start=state0["ring_start"].cpu().numpy(),
+                                          cache_len=state0["cache_len"].cpu().numpy(), next_pos=p,
+                                          n_sink=4)
+            md4s = swa.meta_to_device(m4s, dev)
+            sk4 = torch.zeros(B4, dv["k_new"].shape[1], 4, d4, dtype=dv["q"].dtype, device=dev)
+            sv4 = torch.zeros_like(sk4)
+            f4s = lambda: swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"],
+                                                dv["k_cache"], dv["v_cache"], dv["ring_start"],
+                                                dv["cache_len"], dv["next_pos"], o4, W4, md4s,
+                                                sink_k=sk4, sink_v=sv4)
+            w4s, e4s, _ = timed(f4s, max(5, K // 5), 2, reset=reset4)
+            out["chunk_sink"] = dict(wall_ms=w4s, kernel_ms=e4s,
+                                     flops=4.0 * d4 * m4s["valid_pairs"] * H4)
+            log("chunk sink: wall %.3f ms, event %.3f ms" % (w4s, e4s))
         del dv, o4
 
     # ---------------- ring decode -------------
@@ -404,6 +420,13 @@ def main():
                                       "TFLOP_per_s": round(t, 2),
                                       "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                       "ms_per_step": round(gp["wall_ms"], 4)}
+    if "chunk_sink" in out:
+        cs = out["chunk_sink"]
+        t = cs["flops"] / (cs["wall_ms"] * 1e-3) / 1e12
+        line["chunk_sink"] = {"workload": "chunk workload with 4 attention sinks",
+                              "TFLOP_per_s": round(t, 2),
+                              "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                              "ms_per_step": round(cs["wall_ms"], 4)}
     if "chunk" in out:
         c4 = out["chunk"]
         t = c4["flops"] / (c4["wall_ms"] * 1e-3) / 1e12

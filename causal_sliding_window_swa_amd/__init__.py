@@ -82,8 +82,8 @@ def lib():
             L.swa_bwd_workspace_size.restype = ctypes.c_size_t
             L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
                                   P, P, ctypes.c_size_t, F, P]
-            L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
-                                            P, P, P, P, F, P]
+            L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, P, P, I, I, P, P, P, P, P, P,
+                                            P, P, P, P, P, P, F, P]
             L.swa_decode_workspace_size.argtypes = [I, I, I, I]
             L.swa_decode_workspace_size.restype = ctypes.c_size_t
             L.swa_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -131,8 +131,10 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
                         q_len=None, k_len=None, W_ring=0, ring_start=None, cache_len=None,
                         next_pos=None, n_sink=0):
     """Host metadata build.  Returns dict: cls [B,nqt,nkt] uint8, row_ptr int32,
-    col int32 [nnz], col_cls uint8 [nnz], plus the six statistics."""
-    nk = W_ring + nk_lin
+    col int32 [nnz], col_cls uint8 [nnz], plus the six statistics.  A ring axis
+    with n_sink > 0 starts with n_sink rounded up to tile_k sink slots."""
+    ns = -(-n_sink // tile_k) * tile_k if (W_ring > 0 and n_sink > 0) else 0
+    nk = ns + W_ring + nk_lin
     cls_n, max_nnz = swa_blockmask_size(B, nq, nk, tile_q, tile_k)
     nqt = -(-nq // tile_q)
     nkt = -(-nk // tile_k)
@@ -298,9 +300,18 @@ def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, s
 
 
 def swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,
-                      W, meta, scale=None, stream=None):
+                      W, meta, scale=None, stream=None, n_sink=None, sink_k=None, sink_v=None):
     """Chunked prefill; q,o [B,H,Tq,d], k_new,v_new [B,Hkv,Tq,d], caches [B,Hkv,W,d],
-    ring state int32 [B] device tensors (updated in place on the stream)."""
+    ring state int32 [B] device tensors (updated in place on the stream).
+    Attention sinks: the metadata's n_sink (or n_sink given here) with sink
+    caches sink_k, sink_v [B,Hkv,n_sink,d] (updated in place)."""
+    n_sink = meta.get("n_sink", 0) if n_sink is None else n_sink
+    if n_sink > 0:
+        _require(sink_k is not None and sink_v is not None, "sink caches required")
+        _require(tuple(sink_k.shape) == (q.shape[0], k_new.shape[1], n_sink, q.shape[3]) and
+                 tuple(sink_v.shape) == tuple(sink_k.shape), "sink cache shape")
+        _require(sink_k.is_contiguous() and sink_v.is_contiguous() and
+                 sink_k.dtype == q.dtype and sink_v.dtype == q.dtype, "sink cache layout")
     for t in (q, k_new, v_new, k_cache, v_cache, o, ring_start, cache_len, next_pos):
         _require(t.is_contiguous(), "tensors must be contiguous")
     B, H, Tq, d = q.shape
@@ -310,7 +321,9 @@ def swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, 
     _require(tuple(k_new.shape) == (B, Hkv, Tq, d) and tuple(v_new.shape) == (B, Hkv, Tq, d)
              and tuple(o.shape) == (B, H, Tq, d), "shape mismatch")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    _check(lib().swa_prefill_chunk(_dtype_code(q), B, H, Hkv, Tq, d, W, meta["tile_q"],
+    _check(lib().swa_prefill_chunk(_dtype_code(q), B, H, Hkv, Tq, d, W, n_sink,
+                                   _dptr(sink_k) if n_sink > 0 else None,
+                                   _dptr(sink_v) if n_sink > 0 else None, meta["tile_q"],
                                    meta["tile_k"], _dptr(q), _dptr(k_new), _dptr(v_new),
                                    _dptr(k_cache), _dptr(v_cache), _dptr(ring_start),
                                    _dptr(cache_len), _dptr(next_pos), _dptr(meta["row_ptr"]),

@@ -19,10 +19,12 @@
 namespace {
 
 // Keys at tile offsets [j0, j0+len) hold consecutive logical positions
-// plo, plo+1, ... and are all valid.
+// plo, plo+1, ... and are all valid.  `sink`: the run lies in the sink
+// segment of a ring key axis.
 struct Run {
     int64_t plo;
     int len;
+    bool sink;
 };
 
 // Positions of run r inside [lo, hi].
@@ -34,14 +36,19 @@ inline int64_t count_in(const Run &r, int64_t lo, int64_t hi) {
 
 // Visible keys of a run for a query at logical position t: positions in
 // [t-W+1, t] [M003 §03], plus the sinks [0, min(S-1, t)] ("Sparse attention
-// taxonomy" §3.2), each position counted once.
-inline int64_t overlap(int64_t t, int64_t W, int64_t S, const Run &r) {
+// taxonomy" §3.2), each position counted once.  On a segmented axis (ring
+// with sinks) the sink segment supplies every position below S (visible to
+// any later query) and the other keys count only at positions >= S.
+inline int64_t overlap(int64_t t, int64_t W, int64_t S, bool seg, const Run &r) {
+    if (r.sink) return count_in(r, 0, t);
+    if (seg) return count_in(r, std::max(t - W + 1, S), t);
     int64_t n = count_in(r, t - W + 1, t);
     if (S > 0) n += count_in(r, 0, std::min(S - 1, t)) - count_in(r, t - W + 1, std::min(S - 1, t));
     return n;
 }
 
 struct KeyAxis {
+    int NS, S;  // sink segment length (S rounded up to the key tile) and sinks
     int W_ring, nk_lin;
     int64_t k_start;
     int k_len;
@@ -51,6 +58,11 @@ struct KeyAxis {
     // Runs of valid keys with consecutive positions inside [j0, j1).
     int runs(int j0, int j1, Run *out) const {
         int n = 0;
+        // sink segment: slot s stands for position s, valid below S
+        const int z1 = std::min(std::min(j1, NS), S);
+        if (j0 < z1) out[n++] = Run{j0, z1 - j0, true};
+        j0 = std::max(j0, NS) - NS;
+        j1 = std::max(j1, NS) - NS;
         // ring part: slot s holds position np - cl + ((s - rs) mod W_ring) when
         // that offset is below cl; offsets grow by one per slot except where
         // they wrap at s == rs.
@@ -67,12 +79,12 @@ struct KeyAxis {
                 const int sa = cuts[c], sb = cuts[c + 1];
                 const int ra = ((sa - rs) % W_ring + W_ring) % W_ring;
                 const int len = std::min(sb - sa, cl - ra);
-                if (len > 0) out[n++] = Run{np - cl + ra, len};
+                if (len > 0) out[n++] = Run{np - cl + ra, len, false};
             }
         }
         // linear part: key W_ring + t sits at k_start + t, valid below k_len
         const int b0 = std::max(j0, W_ring) - W_ring, b1 = std::min(j1 - W_ring, k_len);
-        if (b1 > b0) out[n++] = Run{k_start + b0, b1 - b0};
+        if (b1 > b0) out[n++] = Run{k_start + b0, b1 - b0, false};
         return n;
     }
 };
@@ -107,9 +119,6 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink,
     if (!cls || !row_ptr || !col || !col_cls)
         return swa::fail(SWA_EINVAL, "blockmask_build: NULL output array");
     if (n_sink < 0) return swa::fail(SWA_EINVAL, "blockmask_build: n_sink=%d < 0", n_sink);
-    if (n_sink > 0 && W_ring > 0)
-        return swa::fail(SWA_EUNSUPPORTED, "blockmask_build: attention sinks with a ring key "
-                         "axis are not supported");
     if (W_ring > 0) {
         if (W_ring % tile_k != 0)
             return swa::fail(SWA_EINVAL, "blockmask_build: ring size %d not a multiple of "
@@ -117,9 +126,12 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink,
         if (!ring_start || !cache_len || !next_pos)
             return swa::fail(SWA_EINVAL, "blockmask_build: ring state arrays required");
     }
-    if ((int64_t)W_ring + nk_lin > INT_MAX)
+    // a ring axis with sinks starts with a sink segment of whole key tiles
+    const bool seg = W_ring > 0 && n_sink > 0;
+    const int64_t NS = seg ? ((int64_t)n_sink + tile_k - 1) / tile_k * tile_k : 0;
+    if (NS + W_ring + nk_lin > INT_MAX)
         return swa::fail(SWA_EINVAL, "blockmask_build: key axis too long");
-    const int nk = W_ring + nk_lin;
+    const int nk = (int)(NS + W_ring + nk_lin);
     const int nqt = (nq + tile_q - 1) / tile_q;
     const int nkt = (nk + tile_k - 1) / tile_k;
 
@@ -151,6 +163,8 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink,
     Run runs[4];
     for (int b = 0; b < B; b++) {
         KeyAxis ax;
+        ax.NS = (int)NS;
+        ax.S = n_sink;
         ax.W_ring = W_ring;
         ax.nk_lin = nk_lin;
         ax.k_start = k_start ? k_start[b] : 0;
@@ -168,6 +182,14 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink,
             const int nr = ax.runs(0, nk, runs);
             const int64_t last = qs + ql - 1;
             for (int r = 0; r < nr; r++) {
+                if (runs[r].sink) {
+                    st.keys_touched += count_in(runs[r], 0, last);
+                    continue;
+                }
+                if (seg) {
+                    st.keys_touched += count_in(runs[r], std::max<int64_t>(qs - W + 1, n_sink), last);
+                    continue;
+                }
                 st.keys_touched += count_in(runs[r], qs - W + 1, last);
                 if (n_sink > 0)
                     st.keys_touched += count_in(runs[r], 0, std::min<int64_t>(n_sink - 1, last)) -
@@ -195,7 +217,7 @@ extern "C" int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink,
                     if (nr > 0 && near && pmin <= tmax) {
                         for (int i = i0; i < iv1; i++)
                             for (int r = 0; r < nr; r++)
-                                count += overlap(qs + i, W, n_sink, runs[r]);
+                                count += overlap(qs + i, W, n_sink, seg, runs[r]);
                     }
                 }
                 const uint8_t c = count == 0 ? SWA_BLOCK_SKIP

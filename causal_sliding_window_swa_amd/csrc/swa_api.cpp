@@ -214,7 +214,8 @@ extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
 }
 
 extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
-                                 int tile_q, int tile_k, const void *q, const void *k_new,
+                                 int n_sink, void *sink_k, void *sink_v, int tile_q,
+                                 int tile_k, const void *q, const void *k_new,
                                  const void *v_new, void *k_cache, void *v_cache,
                                  int32_t *ring_start_dev, int32_t *cache_len_dev,
                                  int32_t *next_pos_dev, const int32_t *row_ptr_dev,
@@ -225,14 +226,23 @@ extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, in
     int rc;
     if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
     if (Tq < 1 || Tq > W) return fail(SWA_EINVAL, "%s: need 1 <= Tq <= W (Tq=%d W=%d)", fn, Tq, W);
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
     if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
     if (W % tile_k != 0)
         return fail(SWA_EINVAL, "%s: W=%d must be a multiple of tile_k=%d", fn, W, tile_k);
     if ((rc = check_span(fn, dt, W, 2LL * d))) return rc;
+    if ((rc = check_span(fn, dt, n_sink, 2LL * d))) return rc;
+    if ((int64_t)n_sink + tile_k + W > INT_MAX)
+        return fail(SWA_EINVAL, "%s: n_sink=%d too large", fn, n_sink);
     const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o", "row_ptr", "col"};
     if ((rc = check_ptrs(fn, ptrs, names, 8))) return rc;
+    if (n_sink > 0) {
+        const void *sp[] = {sink_k, sink_v};
+        const char *sn[] = {"sink_k", "sink_v"};
+        if ((rc = check_ptrs(fn, sp, sn, 2))) return rc;
+    }
     if (!col_cls_dev || !ring_start_dev || !cache_len_dev || !next_pos_dev)
         return fail(SWA_EINVAL, "%s: col_cls and the ring state arrays are required", fn);
     if (!(scale > 0.f) || scale == INFINITY)
@@ -246,17 +256,23 @@ extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, in
     a.kc = k_cache; a.vc = v_cache;
     a.ring_start = ring_start_dev; a.cache_len = cache_len_dev; a.next_pos = next_pos_dev;
     a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.n_sink = n_sink;
+    a.sk = sink_k; a.sv = sink_v;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
-    // attention reads the old ring; the commit runs after it on the same stream
-    if ((rc = launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s)
-                                          : swa::launch_tile_f32(a, s))))
-        return rc;
-    swa::CommitArgs c;
+    swa::CommitArgs c = {};
     c.B = B; c.Hkv = Hkv; c.Tq = Tq; c.d = d; c.W = W;
     c.elem_bytes = dt == SWA_BF16 ? 2 : 4;
     c.k_new = k_new; c.v_new = v_new; c.kc = k_cache; c.vc = v_cache;
     c.ring_start = ring_start_dev; c.cache_len = cache_len_dev; c.next_pos = next_pos_dev;
+    c.n_sink = n_sink; c.sk = sink_k; c.sv = sink_v;
+    // new rows below n_sink go to the sink caches first (the attention reads
+    // every position below n_sink there); the ring commit runs after the
+    // attention, which reads the old ring
+    if (n_sink > 0 && (rc = launched(fn, swa::launch_sink_write(c, s)))) return rc;
+    if ((rc = launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s)
+                                          : swa::launch_tile_f32(a, s))))
+        return rc;
     return launched(fn, swa::launch_commit(c, s));
 }
 

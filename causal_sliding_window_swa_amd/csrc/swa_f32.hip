@@ -58,7 +58,10 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
     const int d = a.d, nq = a.nq, W = a.W;
     const int g = h / (a.H / a.Hkv);
     const int nqt = (nq + a.tile_q - 1) / a.tile_q;
-    const int nk = (MODE == 1 ? W : 0) + nq;
+    // chunk key axis: [NS sink slots (with sinks) | W ring slots | nq new rows]
+    const int NS =
+        (MODE == 1 && a.n_sink > 0) ? (a.n_sink + a.tile_k - 1) / a.tile_k * a.tile_k : 0;
+    const int nk = (MODE == 1 ? NS + W : 0) + nq;
     // packed batch: sequence b owns tokens cu[b] .. cu[b+1]-1 (token-major)
     const bool pk = MODE == 0 && a.cu;
     const int cub = pk ? a.cu[b] : 0;
@@ -74,6 +77,8 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
     const float *vlin = (const float *)a.v + (pk ? ((size_t)cub * a.Hkv + g) * d : kvh * nq * d);
     const float *kring = (MODE == 1) ? (const float *)a.kc + kvh * W * d : nullptr;
     const float *vring = (MODE == 1) ? (const float *)a.vc + kvh * W * d : nullptr;
+    const float *ksink = NS ? (const float *)a.sk + kvh * a.n_sink * d : nullptr;
+    const float *vsink = NS ? (const float *)a.sv + kvh * a.n_sink * d : nullptr;
     const int e0 = a.row_ptr[b * nqt + qt], e1 = a.row_ptr[b * nqt + qt + 1];
     const int i_end = min(nrows, (qt + 1) * a.tile_q);
 
@@ -92,21 +97,31 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
                     int pos;
                     bool ok;
                     const float *kr, *vr;
-                    if (MODE == 1 && j < W) {
-                        int r = j - rs;
+                    if (MODE == 1 && j < NS) {
+                        // sink slot j holds position j; the chunk's other keys
+                        // below n_sink are skipped, so each position counts once
+                        if (j < a.n_sink && j <= qpos)
+                            st.add(ksink + (size_t)j * d, vsink + (size_t)j * d, d, a.scale);
+                        continue;
+                    }
+                    const int jr = j - NS;
+                    if (MODE == 1 && jr < W) {
+                        int r = jr - rs;
                         r += (r < 0) ? W : 0;
                         ok = r < cl;
                         pos = np - cl + r;
-                        kr = kring + (size_t)j * d;
-                        vr = vring + (size_t)j * d;
+                        kr = kring + (size_t)jr * d;
+                        vr = vring + (size_t)jr * d;
                     } else {
-                        const int t = j - (MODE == 1 ? W : 0);
+                        const int t = jr - (MODE == 1 ? W : 0);
                         pos = ((MODE == 1) ? np : 0) + t;
                         ok = (MODE == 1) ? true : (t < qlen);
                         kr = klin + (size_t)t * krs;
                         vr = vlin + (size_t)t * krs;
                     }
-                    if (ok && pos <= qpos && (pos >= qpos - W + 1 || pos < a.n_sink))
+                    const bool sinkvis = MODE == 0 && pos < a.n_sink;
+                    if (MODE == 1 && pos < a.n_sink) ok = false;  // taken from the sink slots
+                    if (ok && pos <= qpos && (pos >= qpos - W + 1 || sinkvis))
                         st.add(kr, vr, d, a.scale);
                 }
             }
@@ -220,7 +235,7 @@ hipError_t launch_tile_f32(const AttnArgs &a, hipStream_t s) {
 
 // Append (ring write), attend, then advance the ring state.
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s) {
-    CommitArgs c;
+    CommitArgs c = {};
     c.B = a.B;
     c.Hkv = a.Hkv;
     c.Tq = 1;

@@ -31,6 +31,9 @@ struct AttnArgs {
     const int32_t *cu;  // mode 0, may be null: packed batch, sequence b = tokens
                         // cu[b] .. cu[b+1]-1 of token-major q, o [tokens][H][d],
                         // k, v [tokens][Hkv][d]; nq is then the longest sequence
+    // mode 1 with n_sink > 0: sink caches [B][Hkv][n_sink][d]; the key axis is
+    // then [n_sink rounded up to tile_k sink slots | W ring slots | nq new rows]
+    const void *sk, *sv;
     float scale;
 };
 
@@ -52,6 +55,8 @@ struct CommitArgs {
     const void *k_new, *v_new;
     void *kc, *vc;
     int32_t *ring_start, *cache_len, *next_pos;
+    int n_sink;     // sink caches [B][Hkv][n_sink][d] (sk, sv), for launch_sink_write
+    void *sk, *sv;
 };
 
 // bf16 MFMA tile loop (swa_tile_bf16.hip): d in {64,128}, tile_q in {64,128}, tile_k 64.
@@ -87,5 +92,8 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s);
 hipError_t launch_ring_state(const CommitArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
+// Copy the new rows at logical positions below n_sink into the sink caches
+// (before the chunk's attention reads them there).
+hipError_t launch_sink_write(const CommitArgs &a, hipStream_t s);
 
 }  // namespace swa

@@ -48,7 +48,33 @@ __global__ void ring_state_kernel(int32_t *ring_start, int32_t *cache_len, int32
     next_pos[b] = (int32_t)(np + Tq);
 }
 
+// New row t of a chunk sits at logical position next_pos + t; rows below
+// n_sink are also attention sinks ("Sparse attention taxonomy" §3.2) and are
+// copied to sink slot next_pos + t.  grid (min(Tq, n_sink), Hkv, B).
+__global__ void sink_write_kernel(CommitArgs a) {
+    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int64_t pos = (int64_t)a.next_pos[b] + t;
+    if (pos >= a.n_sink) return;
+    const size_t row_bytes = (size_t)a.d * a.elem_bytes;
+    const size_t kvh = (size_t)b * a.Hkv + g;
+    const char *ks = (const char *)a.k_new + (kvh * a.Tq + t) * row_bytes;
+    const char *vs = (const char *)a.v_new + (kvh * a.Tq + t) * row_bytes;
+    char *kd = (char *)a.sk + (kvh * a.n_sink + pos) * row_bytes;
+    char *vd = (char *)a.sv + (kvh * a.n_sink + pos) * row_bytes;
+    for (size_t off = threadIdx.x * 4; off < row_bytes; off += blockDim.x * 4) {
+        *(uint32_t *)(kd + off) = *(const uint32_t *)(ks + off);
+        *(uint32_t *)(vd + off) = *(const uint32_t *)(vs + off);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_sink_write(const CommitArgs &a, hipStream_t s) {
+    if (a.n_sink <= 0) return hipSuccess;
+    dim3 grid(a.Tq < a.n_sink ? a.Tq : a.n_sink, a.Hkv, a.B);
+    hipLaunchKernelGGL(sink_write_kernel, grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s) {
     const int t0 = a.Tq > a.W ? a.Tq - a.W : 0;

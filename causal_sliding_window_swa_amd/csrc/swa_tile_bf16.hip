@@ -79,7 +79,7 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 // Per-request ring/metadata constants of a tile kernel.
 struct KeyPos {
-    int nq, W, nrt, qlen, rs, cl, np;
+    int nq, W, nst, nrt, qlen, rs, cl, np;
 };
 
 // Workgroup p of T runs logical tile L: XCD x = p % 8 gets the contiguous
@@ -123,6 +123,8 @@ void tile_kernel(AttnArgs a) {
     KeyPos kp;
     kp.nq = nq;
     kp.W = a.W;
+    // chunk key axis: [sink tiles (with sinks) | ring tiles | new rows]
+    kp.nst = (MODE == 1 && a.n_sink > 0) ? (a.n_sink + BN - 1) / BN : 0;
     kp.nrt = (MODE == 1) ? a.W / BN : 0;
     // packed batch (PK): sequence b owns tokens cu[b] .. cu[b+1]-1 of a
     // token-major [tokens][heads][D] layout; only its own rows exist
@@ -183,23 +185,32 @@ void tile_kernel(AttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void *)klin, 0, lin_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vlr =
         __builtin_amdgcn_make_buffer_rsrc((void *)vlin, 0, lin_bytes, 0x00020000);
-    __amdgpu_buffer_rsrc_t krr = klr, vrr = vlr;
+    __amdgpu_buffer_rsrc_t krr = klr, vrr = vlr, ksr = klr, vsr = vlr;
     if (MODE == 1) {
         krr = __builtin_amdgcn_make_buffer_rsrc((void *)kring, 0, a.W * ROWB, 0x00020000);
         vrr = __builtin_amdgcn_make_buffer_rsrc((void *)vring, 0, a.W * ROWB, 0x00020000);
+        if (a.n_sink > 0) {  // sink slots past n_sink read as zeros (masked)
+            const size_t sko = kvh * (size_t)a.n_sink * D;
+            ksr = __builtin_amdgcn_make_buffer_rsrc((void *)((const __bf16 *)a.sk + sko), 0,
+                                                    a.n_sink * ROWB, 0x00020000);
+            vsr = __builtin_amdgcn_make_buffer_rsrc((void *)((const __bf16 *)a.sv + sko), 0,
+                                                    a.n_sink * ROWB, 0x00020000);
+        }
     }
     auto issue = [&](int kt, char *kdst) {
         char *vdst = kdst + TILEB;
-        const bool ring = (MODE == 1) && kt < kp.nrt;
-        const int base = ring ? kt * BN * ROWB : (kt - kp.nrt) * BN * RSB;
+        const bool sink = (MODE == 1) && kt < kp.nst;
+        const int kr = kt - kp.nst;
+        const bool ring = (MODE == 1) && !sink && kr < kp.nrt;
+        const int base = sink ? kt * BN * ROWB : ring ? kr * BN * ROWB : (kr - kp.nrt) * BN * RSB;
+        const __amdgpu_buffer_rsrc_t kq = sink ? ksr : ring ? krr : klr;
+        const __amdgpu_buffer_rsrc_t vq = sink ? vsr : ring ? vrr : vlr;
 #pragma unroll
         for (int i = 0; i < LPW; i++) {
             const int ins = wave * LPW + i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? krr : klr,
-                                                     (lds_void *)(kdst + ins * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kq, (lds_void *)(kdst + ins * 1024), 16,
                                                      base + (int)koff[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ring ? vrr : vlr,
-                                                     (lds_void *)(vdst + ins * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vq, (lds_void *)(vdst + ins * 1024), 16,
                                                      base + (int)voff[i], 0, 0, 0);
         }
     };
@@ -229,7 +240,8 @@ void tile_kernel(AttnArgs a) {
     // one tile: compute on `cur` while the next tile streams into `nxt`
     auto tile = [&](int e, const char *cur, char *nxt) {
         const int kt = a.col[e];
-        const bool ragged = (kt - kp.nrt) >= nlin_full;
+        const int kr = kt - kp.nst;  // index on the [ring | new rows] part
+        const bool ragged = (kr - kp.nrt) >= nlin_full;
         const bool partial = (a.col_cls[e] == 2) || ragged;
         __syncthreads();  // this tile is in LDS; every wave is done with the previous one
         if (e + 1 < e1) issue(a.col[e + 1], nxt);
@@ -253,10 +265,15 @@ void tile_kernel(AttnArgs a) {
                     a2 = -base;
                     b2 = min(a.n_sink - 1, min(qpos, qlen - 1)) - base;
                 }
-            } else if (kt < kp.nrt) {
+            } else if (kt < kp.nst) {  // sink slots: position = slot, every one <= qpos
+                a1 = -kt * BN;
+                b1 = min(a.n_sink - 1, qpos) - kt * BN;
+            } else if (kr < kp.nrt) {
                 const int off = kp.np - kp.cl;  // position of ring offset r = 0
-                const int rlo = max(0, lo_pos - off), rhi = min(kp.cl - 1, qpos - off);
-                const int base = kt * BN - kp.rs;  // r of tile key 0, before wrapping
+                // with sinks, positions below n_sink come from the sink slots only
+                const int rlo = max(0, max(lo_pos, a.n_sink) - off);
+                const int rhi = min(kp.cl - 1, qpos - off);
+                const int base = kr * BN - kp.rs;  // r of tile key 0, before wrapping
                 if (base < 0 && base + BN > 0) {   // keys k < -base sit at r = base + k + W
                     two = true;
                     a1 = rlo - base - a.W;
@@ -269,8 +286,8 @@ void tile_kernel(AttnArgs a) {
                     b1 = rhi - rb;
                 }
             } else {
-                const int t0 = (kt - kp.nrt) * BN;  // new-row index of tile key 0
-                a1 = lo_pos - (kp.np + t0);
+                const int t0 = (kr - kp.nrt) * BN;  // new-row index of tile key 0
+                a1 = max(lo_pos, a.n_sink) - (kp.np + t0);
                 b1 = min(qpos - kp.np, nq - 1) - t0;
             }
             if (!qvalid) {

@@ -89,12 +89,18 @@ int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
  * n_sink >= 0 attention sinks [Taxonomy §3.2, the StreamingLLM rule]: keys
  * at logical positions below n_sink stay visible to every query at or after
  * them, besides the window (a key in both counts once); 0 is the plain
- * window.  Sinks need W_ring == 0 (SWA_EUNSUPPORTED otherwise).
+ * window.  With W_ring > 0 the key axis gains a sink segment in front:
+ * [NS sink slots | W_ring ring slots | nk_lin linear keys], NS = n_sink
+ * rounded up to a multiple of tile_k; sink slot s stands for position s
+ * (valid iff s < n_sink) and is visible to every query at or after s, and
+ * ring or linear keys below n_sink are then not counted (the chunk reads
+ * those positions from its sink cache), so each position counts once.
  *
  * For swa_fwd: q_start = k_start = NULL, nq = nk_lin = N, q_len = k_len =
  *   the per-sequence valid lengths (or NULL), W_ring = 0, the call's n_sink.
  * For swa_prefill_chunk: nq = nk_lin = Tq, q_start = k_start = next_pos,
- *   k_len = NULL, W_ring = W and the ring state the call will see.
+ *   k_len = NULL, W_ring = W, the ring state the call will see and the
+ *   call's n_sink; swa_blockmask_size then takes nk = NS + W + Tq.
  *
  * Outputs (caller-owned host memory, sizes from swa_blockmask_size):
  * cls [B][nqt][nkt] uint8, row_ptr [B*nqt+1] int32, col [nnz] int32 (key
@@ -198,12 +204,18 @@ int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
  * formula above yields P) and the state becomes next_pos += Tq,
  * cache_len = min(W, cache_len + Tq), ring_start = slot of the oldest kept
  * position.  Metadata: swa_blockmask_build with W_ring = W, nq = nk_lin = Tq,
- * q_start = k_start = next_pos and the same tiles.
+ * q_start = k_start = next_pos, the same n_sink and the same tiles.
+ * n_sink > 0 [Taxonomy §3.2]: sink_k, sink_v [B][Hkv][n_sink][d] (in/out,
+ * dtype dt) hold the rows of logical positions 0 .. n_sink-1 (as swa_decode
+ * keeps them); new tokens at positions below n_sink are copied there first,
+ * and every query also sees each position below n_sink (at or before its
+ * own) once, from the sink cache.  n_sink == 0: the sink pointers are ignored.
  * Supported: as swa_fwd (W * d * 2 < 2^31 for bf16), plus W % tile_k == 0
  * and 1 <= Tq <= W.
- * Errors: as swa_fwd. */
+ * Errors: as swa_fwd, plus SWA_EINVAL for n_sink < 0 or NULL / misaligned
+ * sink pointers with n_sink > 0. */
 int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
-                      int tile_q, int tile_k,
+                      int n_sink, void *sink_k, void *sink_v, int tile_q, int tile_k,
                       const void *q, const void *k_new, const void *v_new,
                       void *k_cache, void *v_cache,
                       int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,

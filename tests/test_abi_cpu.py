@@ -47,9 +47,10 @@ def test_blockmask_rejects_bad_arguments():
         swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, q_start=[2**31 - 5], k_start=[0])
     with pytest.raises(swa.SwaError):  # negative sink count
         swa.swa_blockmask_build(1, 8, 8, 3, 2, 2, n_sink=-1)
-    with pytest.raises(swa.SwaError):  # sinks with a ring key axis
-        swa.swa_blockmask_build(1, 4, 4, 8, 4, 4, q_start=[8], k_start=[8], W_ring=8,
+    # sinks with a ring key axis: a sink segment of whole key tiles in front
+    m = swa.swa_blockmask_build(1, 4, 4, 8, 4, 4, q_start=[8], k_start=[8], W_ring=8,
                                 ring_start=[0], cache_len=[8], next_pos=[8], n_sink=2)
+    assert m["cls"].shape == (1, 1, (4 + 8 + 4) // 4)
 
 
 P = ctypes.c_void_p
@@ -115,11 +116,12 @@ def test_varlen_validation_codes():
     assert _varlen(d=96) == swa.SWA_EUNSUPPORTED
 
 
-def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False):
+def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False, sink=0, sink_ptr=16):
     p = ctypes.c_void_p(16)
     st = None if nullstate else p
-    return swa.lib().swa_prefill_chunk(0, 1, 4, 2, Tq, d, W, 128, tk, p, p, p, p, p, st, st,
-                                       st, p, p, p, p, ctypes.c_float(0.1), None)
+    sp = ctypes.c_void_p(sink_ptr) if sink_ptr else None
+    return swa.lib().swa_prefill_chunk(0, 1, 4, 2, Tq, d, W, sink, sp, sp, 128, tk, p, p, p, p,
+                                       p, st, st, st, p, p, p, p, ctypes.c_float(0.1), None)
 
 
 def test_chunk_validation_codes():
@@ -128,6 +130,10 @@ def test_chunk_validation_codes():
     assert _chunk(W=96) == swa.SWA_EINVAL  # W not a multiple of tile_k
     assert _chunk(nullstate=True) == swa.SWA_EINVAL
     assert _chunk(d=80) == swa.SWA_EUNSUPPORTED
+    assert _chunk(sink=-1) == swa.SWA_EINVAL
+    assert _chunk(sink=4, sink_ptr=0) == swa.SWA_EINVAL     # sinks need their caches
+    assert _chunk(sink=4, sink_ptr=24) == swa.SWA_EINVAL    # misaligned sink cache
+    assert _chunk(sink=0, sink_ptr=0, nullstate=True) == swa.SWA_EINVAL  # still checks the rest
 
 
 def _decode(H=32, Hkv=8, d=128, W=4096, ws=None, ws_bytes=0, dt=0, sink=0, sink_ptr=16):

@@ -96,3 +96,34 @@ def test_random_small_cases_with_sinks():
 
 def test_prefill_workload_with_sinks():
     both(1, 8192, 8192, 512, 128, 64, n_sink=4)
+
+
+def test_random_ring_cases_with_sinks():
+    """The chunk's key axis with sinks: a sink segment of S slots (rounded up
+    to the key tile) before the ring; rings still filling, full, holding
+    positions below S or not."""
+    rng = np.random.default_rng(2)
+    for _ in range(300):
+        B = int(rng.integers(1, 4))
+        W = int(rng.integers(1, 40))
+        S = int(rng.integers(1, 20))
+        tq = int(rng.integers(1, 9))
+        tk = int(rng.integers(1, 9))
+        Wr = tk * int(rng.integers(1, 6))
+        Tq = int(rng.integers(1, 30))
+        cl = rng.integers(0, Wr + 1, size=B)
+        p = cl + rng.integers(0, 50, size=B)
+        rs = rng.integers(0, Wr, size=B)
+        both(B, Tq, Tq, W, tq, tk, q_start=p, k_start=p, W_ring=Wr, ring_start=rs,
+             cache_len=cl, next_pos=p, n_sink=S)
+
+
+@pytest.mark.parametrize("tq,tk", [(128, 64), (64, 64)])
+def test_chunk_workload_with_sinks(tq, tk):
+    inp = synth.make("chunk", H=1, Hkv=1, d=1)
+    p = inp["next_pos"].numpy()
+    m = both(8, 512, 512, 4096, tq, tk, q_start=p, k_start=p, W_ring=4096,
+             ring_start=inp["ring_start"].numpy(), cache_len=inp["cache_len"].numpy(),
+             next_pos=p, n_sink=4)
+    # every query sees its W window plus 4 sinks far behind it
+    assert m["valid_pairs"] == 8 * 512 * (4096 + 4)

@@ -1,7 +1,8 @@
 """GPU parity of attention sinks ("Sparse attention taxonomy" §3.2: the first
 tokens stay visible besides the last W) through the C ABI against the fp64
 oracle on the same seeded inputs: the full-sequence forward (and its row
-log-sum-exp), streamed decode with a sink cache, and the backward.  Bars as
+log-sum-exp), streamed decode with a sink cache, chunked prefill with a sink
+cache, and the backward.  Bars as
 for the plain window (bf16 max-abs 2e-2, mean-abs 2e-3; fp32 1e-4; caches and
 ring state bit-exact; gradients relative to their largest reference value).
 """
@@ -151,3 +152,104 @@ def test_bwd_sink(dtype, d, tq, tk, W, S):
     check(dq, rq, bf, "sink bwd dq", rel=True)
     check(dk, rk, bf, "sink bwd dk", rel=True)
     check(dv, rv, bf, "sink bwd dv", rel=True)
+
+
+def _chunk_meta(state, Tq, W, S, tq, tk):
+    rs, cl, npos = state[2], state[3], state[4]
+    m = swa.swa_blockmask_build(len(npos), Tq, Tq, W, tq, tk, q_start=npos, k_start=npos,
+                                W_ring=W, ring_start=rs, cache_len=cl, next_pos=npos, n_sink=S)
+    return swa.meta_to_device(m, DEV)
+
+
+@pytest.mark.parametrize("dtype,W,S", [("bf16", 64, 4), ("bf16", 128, 70), ("bf16", 256, 3),
+                                       ("f32", 32, 4), ("f32", 48, 20)])
+def test_chunk_sink_stream(dtype, W, S):
+    """Chunked prefill with sinks mixed with decode steps, from empty rings:
+    chunks that hold sink positions, rings that still hold them, and rings
+    that dropped them.  Every output, and at the end the rings, sink caches
+    and ring state, against the oracle."""
+    d = 128 if dtype == "bf16" else 20
+    tq, tk = (128, 64) if dtype == "bf16" else (32, 16)
+    B, H, Hkv = 3, 8, 2
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(W * 7 + S)
+    kc = torch.zeros(B, Hkv, W, d, dtype=tdt)
+    vc = torch.zeros(B, Hkv, W, d, dtype=tdt)
+    sk = torch.zeros(B, Hkv, S, d, dtype=tdt)
+    sv = torch.zeros(B, Hkv, S, d, dtype=tdt)
+    rs = torch.tensor([0, 5 % W, W - 1], dtype=torch.int32)
+    cl = torch.zeros(B, dtype=torch.int32)
+    npos = torch.zeros(B, dtype=torch.int32)
+    state = [f64(kc), f64(vc), rs.numpy().copy(), cl.numpy().copy(), npos.numpy().copy(),
+             f64(sk), f64(sv)]
+    dev = [x.to(DEV) for x in (kc, vc, rs, cl, npos, sk, sv)]
+    ws = torch.empty(max(16, swa.swa_decode_workspace_size(B, H, d, W)) // 4 + 4,
+                     dtype=torch.float32, device=DEV)
+    sc = 1 / math.sqrt(d)
+    sizes = [3, 1, W // 2, 1, 1, W, 7, 1, W // 3 + 1, W, 2]
+    for step, n in enumerate(sizes):
+        q = (torch.randn(B, H, n, d, generator=gen) * 0.5).to(tdt)
+        kn = (torch.randn(B, Hkv, n, d, generator=gen) * 0.5).to(tdt)
+        vn = (torch.randn(B, Hkv, n, d, generator=gen) * 0.5).to(tdt)
+        where = "chunk sink %s W=%d S=%d step %d (Tq=%d)" % (dtype, W, S, step, n)
+        if n == 1:
+            o = torch.full((B, H, d), float("nan"), dtype=tdt, device=DEV)
+            swa.swa_decode(q[:, :, 0].contiguous().to(DEV), kn[:, :, 0].contiguous().to(DEV),
+                           vn[:, :, 0].contiguous().to(DEV), dev[0], dev[1], dev[2], dev[3],
+                           dev[4], o, ws, W, n_sink=S, sink_k=dev[5], sink_v=dev[6])
+            out = oracle.decode(f64(q[:, :, 0]), f64(kn[:, :, 0]), f64(vn[:, :, 0]), state[0],
+                                state[1], state[2], state[3], state[4], W, sc, n_sink=S,
+                                sink_k=state[5], sink_v=state[6])
+        else:
+            md = _chunk_meta(state, n, W, S, tq, tk)
+            o = torch.full((B, H, n, d), float("nan"), dtype=tdt, device=DEV)
+            swa.swa_prefill_chunk(q.to(DEV), kn.to(DEV), vn.to(DEV), dev[0], dev[1], dev[2],
+                                  dev[3], dev[4], o, W, md, sink_k=dev[5], sink_v=dev[6])
+            out = oracle.chunk(f64(q), f64(kn), f64(vn), state[0], state[1], state[2],
+                               state[3], state[4], W, sc, n_sink=S, sink_k=state[5],
+                               sink_v=state[6])
+        state = list(out[1:])
+        torch.cuda.synchronize()
+        check(o, out[0], dtype == "bf16", where)
+        assert np.array_equal(dev[4].cpu().numpy(), state[4]), where
+    assert np.array_equal(f64(dev[0]), state[0]) and np.array_equal(f64(dev[1]), state[1])
+    assert np.array_equal(dev[2].cpu().numpy(), state[2])
+    assert np.array_equal(dev[3].cpu().numpy(), state[3])
+    assert np.array_equal(dev[4].cpu().numpy(), state[4])
+    assert np.array_equal(f64(dev[5]), state[5]) and np.array_equal(f64(dev[6]), state[6])
+
+
+def test_chunk_sink_workload_two_requests():
+    """The chunk workload (B=8, H=32, Hkv=8, Tq=512, W=4096, full rings far
+    along the sequence) with 4 sinks: all outputs of requests 0 and 5, every
+    ring, sink cache and state."""
+    inp = synth.make("chunk")
+    B, H, Tq, d = inp["q"].shape
+    Hkv, W, S = inp["k_new"].shape[1], 4096, 4
+    gen = torch.Generator().manual_seed(404)
+    sk = (torch.randn(B, Hkv, S, d, generator=gen) * 0.5).to(torch.bfloat16)
+    sv = (torch.randn(B, Hkv, S, d, generator=gen) * 0.5).to(torch.bfloat16)
+    p = inp["next_pos"].numpy()
+    meta = swa.swa_blockmask_build(B, Tq, Tq, W, 128, 64, q_start=p, k_start=p, W_ring=W,
+                                   ring_start=inp["ring_start"].numpy(),
+                                   cache_len=inp["cache_len"].numpy(), next_pos=p, n_sink=S)
+    assert meta["valid_pairs"] == B * Tq * (W + S)
+    md = swa.meta_to_device(meta, DEV)
+    dev = {k: v.to(DEV).contiguous() for k, v in inp.items()}
+    skd, svd = sk.to(DEV), sv.to(DEV)
+    o = torch.full_like(dev["q"], float("nan"))
+    swa.swa_prefill_chunk(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                          dev["ring_start"], dev["cache_len"], dev["next_pos"], o, W, md,
+                          sink_k=skd, sink_v=svd)
+    torch.cuda.synchronize()
+    for b in (0, 5):
+        sl = slice(b, b + 1)
+        out = oracle.chunk(f64(inp["q"][sl]), f64(inp["k_new"][sl]), f64(inp["v_new"][sl]),
+                           f64(inp["k_cache"][sl]), f64(inp["v_cache"][sl]),
+                           inp["ring_start"][sl].numpy(), inp["cache_len"][sl].numpy(),
+                           inp["next_pos"][sl].numpy(), W, 1 / math.sqrt(d), n_sink=S,
+                           sink_k=f64(sk[sl]), sink_v=f64(sv[sl]))
+        check(o[sl], out[0], True, "chunk workload with sinks b=%d" % b)
+        assert np.array_equal(f64(dev["k_cache"][sl]), out[1])
+        assert np.array_equal(f64(skd[sl]), out[6]) and np.array_equal(f64(svd[sl]), out[7])
+    assert np.array_equal(dev["next_pos"].cpu().numpy(), p + Tq)
