@@ -197,14 +197,11 @@ void tile_kernel(AttnArgs a) {
                                                     a.n_sink * ROWB, 0x00020000);
         }
     }
-    auto issue = [&](int kt, char *kdst) {
+    // (a uniform branch per segment: selecting buffer resources by value would
+    // put them in scratch memory)
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t kq, __amdgpu_buffer_rsrc_t vq,
+                         int base, char *kdst) __attribute__((always_inline)) {
         char *vdst = kdst + TILEB;
-        const bool sink = (MODE == 1) && kt < kp.nst;
-        const int kr = kt - kp.nst;
-        const bool ring = (MODE == 1) && !sink && kr < kp.nrt;
-        const int base = sink ? kt * BN * ROWB : ring ? kr * BN * ROWB : (kr - kp.nrt) * BN * RSB;
-        const __amdgpu_buffer_rsrc_t kq = sink ? ksr : ring ? krr : klr;
-        const __amdgpu_buffer_rsrc_t vq = sink ? vsr : ring ? vrr : vlr;
 #pragma unroll
         for (int i = 0; i < LPW; i++) {
             const int ins = wave * LPW + i;
@@ -213,6 +210,15 @@ void tile_kernel(AttnArgs a) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vq, (lds_void *)(vdst + ins * 1024), 16,
                                                      base + (int)voff[i], 0, 0, 0);
         }
+    };
+    auto issue = [&](int kt, char *kdst) {
+        const int kr = kt - kp.nst;
+        if (MODE == 1 && kt < kp.nst)
+            load_tile(ksr, vsr, kt * BN * ROWB, kdst);
+        else if (MODE == 1 && kr < kp.nrt)
+            load_tile(krr, vrr, kr * BN * ROWB, kdst);
+        else
+            load_tile(klr, vlr, (kr - kp.nrt) * BN * RSB, kdst);
     };
 
     // ---- running softmax state: lanes l and l^32 share query column lq
