@@ -419,13 +419,22 @@ void tile_kernel(AttnArgs a) {
                 for (int e2 = 0; e2 < 16; e2++) mloc = fmaxf(mloc, sacc[kb][e2]);
             mloc = half_swap_max(mloc) * c2;
             if (mloc != -INFINITY && (guess || mloc > m_ref)) {
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - mloc);
-                l_run *= alpha;
+                // A guessed reference may move down.  The new one is kept at
+                // or above log2 of the mass already summed (l_run <= 2^32 in
+                // guess mode), so l_run and O shrink or grow to at most 1x and
+                // never overflow; with nothing summed yet there is nothing to
+                // scale (O = l = 0, and exp2 of a large gap would be inf).
+                float mnew = mloc;
+                if (guess && l_run > 0.f) mnew = fmaxf(mnew, m_ref + log2f(l_run));
+                if (l_run > 0.f) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref - mnew);
+                    l_run *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; db++)
+                    for (int db = 0; db < DB; db++)
 #pragma unroll
-                    for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
-                m_ref = mloc;
+                        for (int e2 = 0; e2 < 16; e2++) oacc[db][e2] *= alpha;
+                }
+                m_ref = mnew;
                 guess = false;
             }
             psum = probs();
