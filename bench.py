@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list: prefill,gqa,chunk,decode,bwd,sink")
+                    help="comma list: prefill,gqa,chunk,decode,bwd,sink,variants")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(scale for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -80,7 +80,7 @@ def main():
     from causal_sliding_window_swa_amd import synth
 
     only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode",
-                                                         "bwd", "sink"}
+                                                         "bwd", "sink", "variants"}
     dev = torch.device("cuda:0")
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -96,24 +96,50 @@ def main():
     K, WU = args.steps, args.warmup
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
+    SETTLE_S = 0.25
+
     def timed(fn, steps, warmup, reset=None, graph=True):
         """(ms per step, mean event-timed ms per step, eager wall ms per step).
+
         The first figure is the wall time of one replay of a HIP graph holding
-        the `steps` steps (captured once, after the eager runs), so that the
-        host's per-launch cost between steps is not counted; with graph=False
-        (steps with host work) it is the eager wall time."""
-        for _ in range(warmup):
+        the `steps` steps, bracketed by device synchronisations, so that the
+        host's per-launch cost between steps is not counted.  The GPU lowers
+        its clocks within milliseconds of going idle and needs tens of
+        milliseconds of load to raise them again (graph capture and
+        instantiation leave it idle), so after the `warmup` eager steps and
+        the capture the graph is replayed, untimed, for SETTLE_S seconds
+        before the timed replay; the event-timed and eager passes follow
+        while the GPU is still busy.  graph=False (steps with host work): the
+        eager wall time only."""
+        def step():
             if reset:
                 reset()
             fn()
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        if not graph:
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3 / steps
+            return wall, wall, wall
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                step()
+        g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            if reset:
-                reset()
-            fn()
+        while time.perf_counter() - t0 < SETTLE_S:
+            g.replay()
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
+        gms = (time.perf_counter() - t0) * 1e3 / steps
+        del g
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for s, e in evs:
@@ -124,21 +150,11 @@ def main():
             e.record(stream)
         torch.cuda.synchronize()
         ev = sum(s.elapsed_time(e) for s, e in evs) / steps
-        if not graph:
-            return wall, ev, wall
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(steps):
-                if reset:
-                    reset()
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        g.replay()
+        for _ in range(steps):
+            step()
         torch.cuda.synchronize()
-        gms = (time.perf_counter() - t0) * 1e3 / steps
-        del g
+        wall = (time.perf_counter() - t0) * 1e3 / steps
         return gms, ev, wall
 
     out = {}
@@ -172,6 +188,37 @@ def main():
     prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, eager_ms=eager_ms, flops=flops,
                    meta_ms=t_meta, meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
     out["prefill"] = prefill
+
+    # ---------------- prefill variants: 64-row tiles, cold caches, W = N -------------
+    if "variants" in only:
+        m64 = swa.swa_blockmask_build(B, N, N, W, 64, 64)
+        md64 = swa.meta_to_device(m64, dev)
+        w64, e64, _ = timed(lambda: swa.swa_fwd(q, k, v, o, W, md64), K, WU)
+        prefill["tile64"] = dict(wall_ms=w64, kernel_ms=e64, n_live=m64["n_live"],
+                                 covered=m64["covered_coords"])
+        log("prefill tile 64: graph %.4f ms/step, event %.4f ms" % (w64, e64))
+        # cold caches: 1 GiB written between launches evicts L2 and the
+        # 256 MB Infinity Cache; only the kernel is inside the events
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for i, (s_, e_) in enumerate(evs):
+            flush.fill_(float(i))
+            s_.record(stream)
+            fwd()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        cold = sorted(s_.elapsed_time(e_) for s_, e_ in evs)
+        prefill["cold"] = dict(median_ms=cold[K // 2], min_ms=cold[0])
+        del flush
+        log("prefill cold: median %.4f ms, min %.4f ms" % (cold[K // 2], cold[0]))
+        # skipping check: W = N is dense causal, with 8.26x the visible pairs
+        mden = swa.swa_blockmask_build(B, N, N, N, tq, tk)
+        mdd = swa.meta_to_device(mden, dev)
+        _, eden, _ = timed(lambda: swa.swa_fwd(q, k, v, o, N, mdd), max(3, K // 10), 2)
+        prefill["dense"] = dict(kernel_ms=eden, valid_pairs=mden["valid_pairs"])
+        log("prefill at W=N: event %.4f ms" % eden)
+        del mdd, md64
 
     # ---------------- backward on the prefill workload -------------
     if "bwd" in only:
@@ -339,6 +386,7 @@ def main():
         "steps": K,
         "warmup": WU,
         "ms_per_step": round(pf["wall_ms"], 5),
+        "settle_s_before_timing": SETTLE_S,
         "eager_ms_per_step": round(pf["eager_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -365,6 +413,37 @@ def main():
                      "covered_coords": pf["stats"]["covered_coords"]},
         "cpu_baseline": cpu,
     }
+    # the fraction of the computed tile area that holds visible pairs
+    line["roofline"]["useful_fraction_of_covered"] = round(
+        pf["stats"]["valid_pairs"] / pf["stats"]["covered_coords"], 4)
+    # the same launch against the HBM roofline: Q, K, V, O once
+    alg_bytes = 4.0 * B * H * N * d * 2
+    line["prefill_hbm"] = {"algorithmic_bytes": int(alg_bytes),
+                           "GB_per_s": round(alg_bytes / (pf["kernel_ms"] * 1e-3) / 1e9, 1),
+                           "pct_of_peak": round(100 * alg_bytes / (pf["kernel_ms"] * 1e-3) /
+                                                1e9 / PEAK_HBM_GBS, 2)}
+    if "tile64" in pf:
+        t64 = pf["tile64"]
+        line["prefill_tile64"] = {
+            "workload": "prefill workload with 64x64 tiles (%d live tiles)" % t64["n_live"],
+            "TFLOP_per_s": round(pf["flops"] / (t64["wall_ms"] * 1e-3) / 1e12, 2),
+            "kernel_TFLOP_per_s": round(pf["flops"] / (t64["kernel_ms"] * 1e-3) / 1e12, 2),
+            "ms_per_step": round(t64["wall_ms"], 5),
+            "useful_fraction_of_covered": round(pf["stats"]["valid_pairs"] / t64["covered"], 4)}
+    if "cold" in pf:
+        line["prefill_cold_caches"] = {
+            "workload": "prefill workload, 1 GiB written between launches (L2 and Infinity "
+                        "Cache evicted)",
+            "median_ms": round(pf["cold"]["median_ms"], 5),
+            "min_ms": round(pf["cold"]["min_ms"], 5),
+            "TFLOP_per_s": round(pf["flops"] / (pf["cold"]["median_ms"] * 1e-3) / 1e12, 2)}
+    if "dense" in pf:
+        dn = pf["dense"]
+        line["skip_check"] = {
+            "workload": "prefill workload at W = N (dense causal)",
+            "kernel_ms": round(dn["kernel_ms"], 4),
+            "time_ratio": round(dn["kernel_ms"] / pf["kernel_ms"], 2),
+            "pair_ratio": round(dn["valid_pairs"] / pf["stats"]["valid_pairs"], 2)}
     if "decode" in out:
         dd = out["decode"]
         gbs = dd["kv_bytes"] / (dd["wall_ms"] * 1e-3) / 1e9
