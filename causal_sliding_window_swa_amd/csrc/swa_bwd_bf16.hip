@@ -383,7 +383,10 @@ void dkdv_kernel(BwdArgs a) {
         const char *dsm = cur + TILEB;
         const float *lsm = (const float *)(cur + 2 * TILEB);
         const float *Dsm = lsm + 64;
-#pragma unroll
+        // the two 32-row blocks run as a loop: unrolled, the compiler hoisted
+        // both blocks' LDS fragments and addresses and spilled 48 registers
+        // (with them in the loop: 181 VGPRs + the AGPRs, no scratch)
+#pragma unroll 1
         for (int rb = 0; rb < 2; rb++) {
             __builtin_amdgcn_sched_barrier(0);
             f32x16 s, dp;
