@@ -69,7 +69,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only; --gpus %d is not supported "
-                         "(the per-GPU kernels need no communication; see DESIGN.md)\n"
+                         "(each request and KV head is an independent unit, so a sharded run "
+                         "would need no communication; no multi-GPU path is built)\n"
                          % args.gpus)
         sys.exit(2)
     import numpy as np

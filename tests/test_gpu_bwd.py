@@ -1,8 +1,9 @@
 """GPU parity of the backward (swa_bwd) and of the forward's row log-sum-exp,
 through the C ABI, against the fp64 oracle on the same seeded inputs.
 
-Bars (derived in the design doc from the arithmetic): gradients are compared after
-dividing by their reference's largest magnitude (at least 1): bf16 inputs
+Bars, from the arithmetic (bf16 operands in every product, fp32 accumulation):
+gradients are compared after dividing by their reference's largest magnitude
+(at least 1): bf16 inputs
 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32 path max-abs <= 1e-4; lse abs
 <= 4e-3 (bf16: the row sum is taken over bf16-rounded P) or 1e-5 (fp32);
 padded rows and keys exactly 0.
