@@ -98,6 +98,7 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
     SETTLE_S = 0.25
+    last_events = []  # per-launch event times (ms) of the latest timed() call
 
     def timed(fn, steps, warmup, reset=None, graph=True):
         """(ms per step, mean event-timed ms per step, eager wall ms per step).
@@ -150,7 +151,8 @@ def main():
             fn()
             e.record(stream)
         torch.cuda.synchronize()
-        ev = sum(s.elapsed_time(e) for s, e in evs) / steps
+        last_events[:] = sorted(s.elapsed_time(e) for s, e in evs)
+        ev = sum(last_events) / steps
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
@@ -178,6 +180,7 @@ def main():
     flops = 4.0 * d * meta["valid_pairs"] * H
     fwd = lambda: swa.swa_fwd(q, k, v, o, W, md)
     wall_ms, ev_ms, eager_ms = timed(fwd, K, WU)
+    ev_median, ev_min = last_events[K // 2], last_events[0]
     log("prefill: graph %.4f ms/step, eager %.4f ms/step, event %.4f ms/launch" % (
         wall_ms, eager_ms, ev_ms))
     # end to end with the metadata rebuilt and copied each step
@@ -186,7 +189,8 @@ def main():
         mdd = swa.meta_to_device(m, dev)
         swa.swa_fwd(q, k, v, o, W, mdd)
     e2e_ms, _, _ = timed(fwd_with_meta, max(5, K // 5), 2, graph=False)
-    prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, eager_ms=eager_ms, flops=flops,
+    prefill = dict(wall_ms=wall_ms, kernel_ms=ev_ms, kernel_ms_median=ev_median,
+                   kernel_ms_min=ev_min, eager_ms=eager_ms, flops=flops,
                    meta_ms=t_meta, meta_h2d_ms=t_h2d, e2e_ms=e2e_ms, stats=meta)
     out["prefill"] = prefill
 
@@ -404,7 +408,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counters_for("swa_fwd_prefill", tile_digest),
                      "kernel": "swa::tile_kernel<0,128,4> (swa_fwd)",
-                     "kernel_ms": round(pf["kernel_ms"], 5)},
+                     "kernel_ms": round(pf["kernel_ms"], 5),
+                     "kernel_ms_median": round(pf["kernel_ms_median"], 5),
+                     "kernel_ms_min": round(pf["kernel_ms_min"], 5)},
         "metadata": {"build_ms": round(pf["meta_ms"], 4), "h2d_ms": round(pf["meta_h2d_ms"], 4),
                      "e2e_ms_per_step_with_build": round(pf["e2e_ms"], 4),
                      "e2e_TFLOPs_with_build": round(pf["flops"] / (pf["e2e_ms"] * 1e-3) / 1e12,
