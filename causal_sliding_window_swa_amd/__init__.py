@@ -152,7 +152,8 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
     nnz = int(row_ptr[-1])
     out = {"cls": cls[:cls_n].reshape(B, nqt, nkt), "row_ptr": row_ptr,
            "col": col[:nnz].copy(), "col_cls": col_cls[:nnz].copy(),
-           "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink, "max_len": nq}
+           "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink, "max_len": nq,
+           "B": B, "nq": nq, "nk_lin": nk_lin, "W": W, "W_ring": W_ring}
     out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
     return out
 
@@ -199,7 +200,29 @@ def meta_to_device(meta, device):
             "col_cls": torch.from_numpy(ccls).to(dev),
             "cls": torch.from_numpy(np.ascontiguousarray(meta["cls"]).reshape(-1)).to(dev),
             "tile_q": meta["tile_q"], "tile_k": meta["tile_k"],
-            "n_sink": meta.get("n_sink", 0), "max_len": meta.get("max_len", 0)}
+            "n_sink": meta.get("n_sink", 0), "max_len": meta.get("max_len", 0),
+            **{k: meta[k] for k in _SHAPE_KEYS}}
+
+
+_SHAPE_KEYS = ("B", "nq", "nk_lin", "W", "W_ring")
+
+
+def _check_meta(meta, fn, **want):
+    """The kernels index the device metadata without bounds checks, so it must
+    come from a swa_blockmask_build with the call's shape; a mismatch is
+    rejected here, before anything is enqueued."""
+    for key in _SHAPE_KEYS:
+        if key not in meta:
+            raise SwaError(SWA_EINVAL, "%s: metadata lacks %r (use swa_blockmask_build and "
+                           "meta_to_device)" % (fn, key))
+    for key, v in want.items():
+        if meta[key] != v:
+            raise SwaError(SWA_EINVAL, "%s: metadata built for %s=%d, the call has %s=%d"
+                           % (fn, key, meta[key], key, v))
+    nqt = -(-meta["nq"] // meta["tile_q"])
+    if meta["row_ptr"].numel() != meta["B"] * nqt + 1:
+        raise SwaError(SWA_EINVAL, "%s: row_ptr has %d entries, the build's shape needs %d"
+                       % (fn, meta["row_ptr"].numel(), meta["B"] * nqt + 1))
 
 
 def _dptr(t):
@@ -237,6 +260,7 @@ def swa_fwd(q, k, v, o, W, meta, q_len=None, lse=None, scale=None, stream=None):
     _require(tuple(k.shape) == (B, Hkv, N, d) and tuple(v.shape) == (B, Hkv, N, d) and
              tuple(o.shape) == (B, H, N, d), "shape mismatch")
     _require(k.dtype == q.dtype == v.dtype == o.dtype, "dtype mismatch")
+    _check_meta(meta, "swa_fwd", B=B, nq=N, nk_lin=N, W=W, W_ring=0)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().swa_fwd(_dtype_code(q), B, H, Hkv, N, d, W, meta.get("n_sink", 0),
                          meta["tile_q"], meta["tile_k"],
@@ -259,6 +283,9 @@ def swa_fwd_varlen(q, k, v, o, W, meta, cu_seqlens, lse=None, scale=None, stream
              tuple(o.shape) == (total, H, d), "shape mismatch")
     _require(k.dtype == q.dtype == v.dtype == o.dtype, "dtype mismatch")
     B = cu_seqlens.numel() - 1
+    _check_meta(meta, "swa_fwd_varlen", B=B, W=W, W_ring=0)
+    _require(meta["nk_lin"] == meta["nq"], "swa_fwd_varlen: metadata must be built with "
+             "nq = nk_lin = max_len")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().swa_fwd_varlen(_dtype_code(q), B, H, Hkv, total, meta["max_len"], d, W,
                                 meta.get("n_sink", 0), meta["tile_q"], meta["tile_k"],
@@ -288,6 +315,10 @@ def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, s
              tuple(dv.shape) == (B, Hkv, N, d) and tuple(lse.shape) == (B, H, N),
              "shape mismatch")
     _require(len({t.dtype for t in (q, k, v, o, dout, dq, dk, dv)}) == 1, "dtype mismatch")
+    _check_meta(meta, "swa_bwd", B=B, nq=N, nk_lin=N, W=W, W_ring=0)
+    nkt = -(-N // meta["tile_k"])
+    _require(meta["cls"].numel() == B * (-(-N // meta["tile_q"])) * nkt,
+             "swa_bwd: class grid size does not match the call")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().swa_bwd(_dtype_code(q), B, H, Hkv, N, d, W, meta.get("n_sink", 0),
@@ -320,6 +351,9 @@ def swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, 
              "cache shape must be [B,Hkv,W,d]")
     _require(tuple(k_new.shape) == (B, Hkv, Tq, d) and tuple(v_new.shape) == (B, Hkv, Tq, d)
              and tuple(o.shape) == (B, H, Tq, d), "shape mismatch")
+    _check_meta(meta, "swa_prefill_chunk", B=B, nq=Tq, nk_lin=Tq, W=W, W_ring=W)
+    _require(n_sink == meta.get("n_sink", 0), "swa_prefill_chunk: metadata built for "
+             "n_sink=%d, the call has %d" % (meta.get("n_sink", 0), n_sink))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().swa_prefill_chunk(_dtype_code(q), B, H, Hkv, Tq, d, W, n_sink,
                                    _dptr(sink_k) if n_sink > 0 else None,

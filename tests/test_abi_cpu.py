@@ -173,3 +173,50 @@ def test_bf16_span_limit():
     rc = L.swa_fwd(1, 1, 1, 1, 1 << 23, 128, 64, 0, 128, 64, P, P, P, P, None, P, P, P, None,
                    ctypes.c_float(0.1), None)
     assert b"span" not in L.swa_last_error()
+
+
+def test_binding_rejects_mismatched_metadata():
+    """The kernels index the device metadata without bounds checks; the
+    binding refuses metadata built for another shape before any launch
+    (CPU tensors: nothing reaches the library)."""
+    import torch
+    bf = torch.bfloat16
+    meta = swa.meta_to_device(swa.swa_blockmask_build(1, 128, 128, 16, 128, 64), "cpu")
+    q = torch.zeros(1, 4, 256, 128, dtype=bf)
+    k = torch.zeros(1, 2, 256, 128, dtype=bf)
+    with pytest.raises(swa.SwaError, match="nq=128"):
+        swa.swa_fwd(q, k, k.clone(), q.clone(), 16, meta)  # N = 256 against a build for 128
+    q, k = q[:, :, :128].contiguous(), k[:, :, :128].contiguous()
+    with pytest.raises(swa.SwaError, match="W=16"):
+        swa.swa_fwd(q, k, k.clone(), q.clone(), 32, meta)
+    q2, k2 = torch.cat([q, q]), torch.cat([k, k])
+    with pytest.raises(swa.SwaError, match="B=1"):
+        swa.swa_fwd(q2, k2, k2.clone(), q2.clone(), 16, meta)
+    lse = torch.zeros(1, 4, 128)
+    ws = torch.zeros(swa.swa_bwd_workspace_size(1, 4, 128) // 4)
+    with pytest.raises(swa.SwaError, match="W=16"):
+        swa.swa_bwd(q, k, k.clone(), q.clone(), q.clone(), lse, q.clone(), k.clone(), k.clone(),
+                    ws, 8, meta)
+    # a chunk needs ring metadata of its own W and Tq
+    with pytest.raises(swa.SwaError, match="W_ring=0"):
+        swa.swa_prefill_chunk(torch.zeros(1, 4, 64, 128, dtype=bf),
+                              torch.zeros(1, 2, 64, 128, dtype=bf),
+                              torch.zeros(1, 2, 64, 128, dtype=bf),
+                              torch.zeros(1, 2, 128, 128, dtype=bf),
+                              torch.zeros(1, 2, 128, 128, dtype=bf),
+                              torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                              torch.zeros(1, dtype=torch.int32),
+                              torch.zeros(1, 4, 64, 128, dtype=bf), 128,
+                              swa.meta_to_device(swa.swa_blockmask_build(1, 64, 64, 128, 128, 64),
+                                                 "cpu"))
+    # varlen: a build for another batch size
+    cu = torch.tensor([0, 50, 100], dtype=torch.int32)
+    mv = swa.meta_to_device(swa.swa_blockmask_build(3, 60, 60, 16, 128, 64), "cpu")
+    t = torch.zeros(100, 4, 128, dtype=bf)
+    kv = torch.zeros(100, 2, 128, dtype=bf)
+    with pytest.raises(swa.SwaError, match="B=3"):
+        swa.swa_fwd_varlen(t, kv, kv.clone(), t.clone(), 16, mv, cu)
+    # a hand-made dict without the build's shape is refused too
+    bad = {x: meta[x] for x in ("row_ptr", "col", "col_cls", "cls", "tile_q", "tile_k")}
+    with pytest.raises(swa.SwaError, match="lacks"):
+        swa.swa_fwd(q, k, k.clone(), q.clone(), 16, bad)
