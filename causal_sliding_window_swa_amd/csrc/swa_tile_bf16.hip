@@ -244,13 +244,34 @@ void tile_kernel(AttnArgs a) {
     const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);  // + db*32
 
     // one tile: compute on `cur` while the next tile streams into `nxt`
+    // Metadata entries travel one tile ahead of their use: tile e's column and
+    // class are loaded during tile e-1, the column of tile e+1 (whose K/V this
+    // tile issues) one tile earlier still.  They are loaded per lane at an
+    // address the compiler cannot prove uniform (lz is an opaque 0), so the
+    // values stay in vector registers and the wait for them falls where
+    // readfirstlane takes them, a tile later, instead of right after the load.
+    int lz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+    int v_col = 0, v_col1 = 0, v_cls = 0;
+    if (e1 > e0) {
+        v_col = a.col[e0 + lz];
+        v_cls = a.col_cls[e0 + lz];
+        v_col1 = (e0 + 1 < e1) ? a.col[e0 + 1 + lz] : 0;
+    }
     auto tile = [&](int e, const char *cur, char *nxt) {
-        const int kt = a.col[e];
+        const int kt = __builtin_amdgcn_readfirstlane(v_col);
+        const int kt1 = __builtin_amdgcn_readfirstlane(v_col1);
+        const int cls = __builtin_amdgcn_readfirstlane(v_cls);
         const int kr = kt - kp.nst;  // index on the [ring | new rows] part
         const bool ragged = (kr - kp.nrt) >= nlin_full;
-        const bool partial = (a.col_cls[e] == 2) || ragged;
+        const bool partial = (cls == 2) || ragged;
         __syncthreads();  // this tile is in LDS; every wave is done with the previous one
-        if (e + 1 < e1) issue(a.col[e + 1], nxt);
+        if (e + 1 < e1) issue(kt1, nxt);
+        // loads for the next tiles (after the barrier, so that its wait does
+        // not include them)
+        v_col = v_col1;
+        v_col1 = (e + 2 < e1) ? a.col[e + 2 + lz] : 0;
+        v_cls = (e + 1 < e1) ? a.col_cls[e + 1 + lz] : 0;
         const char *ksm = cur;
         const char *vsm = cur + TILEB;
 
@@ -467,7 +488,7 @@ void tile_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_s_setprio(0);
     };
-    if (e1 > e0) issue(a.col[e0], stage0);
+    if (e1 > e0) issue(__builtin_amdgcn_readfirstlane(v_col), stage0);
     for (int e = e0; e < e1; e += 2) {
         tile(e, stage0, stage1);
         if (e + 1 < e1) tile(e + 1, stage1, stage0);
