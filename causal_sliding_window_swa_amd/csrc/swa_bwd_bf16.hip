@@ -11,7 +11,8 @@
 // LDS, double-buffered).  Per tile: S^T = K Q^T and dP^T = V dO^T (A = K or
 // V rows read from LDS, B = the wave's Q or dO rows in registers), then
 // dS^T = P^T (dP^T - D) and dQ^T += K^T dS^T with K^T read by transposing
-// LDS reads.  Each lane holds one query column: lse and D are per lane.
+// LDS reads, one 32-key half after the other (so that two waves fit per
+// SIMD).  Each lane holds one query column: lse and D are per lane.
 //
 // dkdv_kernel: one workgroup per (key tile of 64, kv head, request), 32 keys
 // per wave held in registers, visiting 64-row steps of every query head of
@@ -124,7 +125,7 @@ __device__ __forceinline__ void stage_vals(const float *src, int i, int n, char 
 
 // ---------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel(BwdArgs a) {
     constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
     __shared__ __attribute__((aligned(1024))) char stage0[2 * TILEB];
@@ -197,10 +198,24 @@ void dq_kernel(BwdArgs a) {
     const int tr_row = 4 * hh + (tr_j >> 2);
     const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);
 
+    // CSR columns travel one tile ahead of their use, in vector registers
+    // (loaded at an address the compiler cannot prove uniform, lz an opaque
+    // 0), so that no tile waits at its barrier for a global load; see the
+    // forward tile kernel
+    int lz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+    int v_col = 0, v_col1 = 0;
+    if (e1 > e0) {
+        v_col = a.col[e0 + lz];
+        v_col1 = (e0 + 1 < e1) ? a.col[e0 + 1 + lz] : 0;
+    }
     auto tile = [&](int e, const char *cur, char *nxt) __attribute__((always_inline)) {
-        const int kt = a.col[e];
+        const int kt = __builtin_amdgcn_readfirstlane(v_col);
+        const int kt1 = __builtin_amdgcn_readfirstlane(v_col1);
         __syncthreads();
-        if (e + 1 < e1) issue(a.col[e + 1], nxt);
+        if (e + 1 < e1) issue(kt1, nxt);
+        v_col = v_col1;
+        v_col1 = (e + 2 < e1) ? a.col[e + 2 + lz] : 0;
         const char *ksm = cur;
         const char *vsm = cur + TILEB;
         // visible keys of this lane's row inside the tile: [a1, b1] (tile-local)
@@ -221,47 +236,50 @@ void dq_kernel(BwdArgs a) {
         const int L2 = empty2 ? -(1 << 20) : a2 - 4 * hh;
         const uint32_t n2 = empty2 ? 0u : (uint32_t)(b2 - a2);
 
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; kb2++)
+        // the two 32-key halves one after the other (a loop, not unrolled): S,
+        // dP and dS of one half are live at a time, which keeps the kernel
+        // within the 256 registers of two waves per SIMD
+#pragma unroll 1
+        for (int kb2 = 0; kb2 < 2; kb2++) {
+            f32x16 s, dp;
 #pragma unroll
             for (int e2 = 0; e2 < 16; e2++) {
-                s[kb2][e2] = 0.f;
-                dp[kb2][e2] = 0.f;
+                s[e2] = 0.f;
+                dp[e2] = 0.f;
             }
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; kb2++) {
-                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    row_frag<D>(ksm, kb2 * 32, lq, hh, ks), qf[ks], s[kb2], 0, 0, 0);
-                dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    row_frag<D>(vsm, kb2 * 32, lq, hh, ks), dof[ks], dp[kb2], 0, 0, 0);
+            for (int ks = 0; ks < KS; ks++) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ksm, kb2 * 32, lq, hh, ks),
+                                                            qf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vsm, kb2 * 32, lq, hh, ks),
+                                                             dof[ks], dp, 0, 0, 0);
             }
-        // dS^T packed as B operands: dsk[kk] for 16-key step kk (key 16kk + 8r + 4hh + t)
-        bf16x8 dsk[4];
+            // dS^T packed as B operands: dsk[s2] for 16-key step 2*kb2 + s2
+            // (key 16kk + 8r + 4hh + t)
+            bf16x8 dsk[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            const int kb2 = kk >> 1, s2 = kk & 1;
+            for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-            for (int r = 0; r < 2; r++)
+                for (int r = 0; r < 2; r++)
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const int e2 = (2 * s2 + r) * 4 + t;
-                    const int c = kb2 * 32 + 8 * (2 * s2 + r) + t;  // minus 4hh, see L1
-                    const bool vis = ((uint32_t)(c - L1) <= n1) | ((uint32_t)(c - L2) <= n2);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb2][e2], c2, -lse2)) : 0.f;
-                    dsk[kk][4 * r + t] = (__bf16)(p * (dp[kb2][e2] - Dr));
-                }
+                    for (int t = 0; t < 4; t++) {
+                        const int e2 = (2 * s2 + r) * 4 + t;
+                        const int c = kb2 * 32 + 8 * (2 * s2 + r) + t;  // minus 4hh, see L1
+                        const bool vis = ((uint32_t)(c - L1) <= n1) | ((uint32_t)(c - L2) <= n2);
+                        const float p =
+                            vis ? __builtin_amdgcn_exp2f(fmaf(s[e2], c2, -lse2)) : 0.f;
+                        dsk[s2][4 * r + t] = (__bf16)(p * (dp[e2] - Dr));
+                    }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+                for (int db = 0; db < DB; db++)
+                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_frag<D>(ksm, 2 * kb2 + s2, db, tr_row, tr_col), dsk[s2], dqacc[db], 0, 0,
+                        0);
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++)
-#pragma unroll
-            for (int db = 0; db < DB; db++)
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    tr_frag<D>(ksm, kk, db, tr_row, tr_col), dsk[kk], dqacc[db], 0, 0, 0);
     };
-    if (e1 > e0) issue(a.col[e0], stage0);
+    if (e1 > e0) issue(__builtin_amdgcn_readfirstlane(v_col), stage0);
     for (int e = e0; e < e1; e += 2) {
         tile(e, stage0, stage1);
         if (e + 1 < e1) tile(e + 1, stage1, stage0);
@@ -341,10 +359,27 @@ void dkdv_kernel(BwdArgs a) {
     // step index t over (h, qt, sub); returns the next live step at or after t
     const int qtn = qt_hi - qt_lo + 1;
     const int nsteps = G * qtn * spt;
+    // the class-grid column of this key tile over [qt_lo, qt_hi], read once
+    // into two wave-wide masks (live, partial) when it spans at most 64 query
+    // tiles; the step loop then never waits on a global load for it
+    const bool inmask = qtn <= 64;
+    uint64_t m_live = 0, m_part = 0;
+    if (inmask) {
+        const int c = lane < qtn ? clsb[(size_t)(qt_lo + lane) * nkt + kt] : 0;
+        m_live = __ballot(c != 0);
+        m_part = __ballot(c == 2);
+    }
+    auto cls_of = [&](int qt) __attribute__((always_inline)) -> int {
+        if (inmask) {
+            const int r = qt - qt_lo;
+            return ((m_live >> r) & 1) ? (((m_part >> r) & 1) ? 2 : 1) : 0;
+        }
+        return clsb[(size_t)qt * nkt + kt];
+    };
     auto live_from = [&](int t) __attribute__((always_inline)) -> int  {
         for (; t < nsteps; t++) {
             const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
-            if (clsb[(size_t)qt * nkt + kt] != 0 && qt * tq + sub * BN < N) break;
+            if (cls_of(qt) != 0 && qt * tq + sub * BN < N) break;
         }
         return t;
     };
@@ -354,7 +389,7 @@ void dkdv_kernel(BwdArgs a) {
         s0 = qt * tq + sub * BN;
         // a full class counts only in-range pairs: steps or key tiles cut by
         // the array edge are masked too
-        part = clsb[(size_t)qt * nkt + kt] == 2 || s0 + BN > N || kt * BN + BN > N;
+        part = cls_of(qt) == 2 || s0 + BN > N || kt * BN + BN > N;
     };
     auto issue = [&](int t, char *dst) __attribute__((always_inline)) {
         int hq, s0;
