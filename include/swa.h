@@ -2,9 +2,11 @@
  * swa.h -- C ABI of the MI355X (gfx950) causal sliding-window attention library.
  *
  * The operation (cited by page title and section):
- *   [M003] "Weight sparsity vs attention sparsity" (AI-infra KB), §03-§06
+ *   [M003] "Weight sparsity vs attention sparsity" (AI-infra KB), §03-§08
  *   [Ch10] "LLMs from scratch, chapter 10: SWA and DSA", §10.1-§10.2
- *   [Blog] "Dense attention vs sliding-window sparse attention", §3.2
+ *   [Blog] "Dense attention vs sliding-window sparse attention", §3.1-§3.3, §5.2
+ *   [Taxonomy] "Sparse attention taxonomy: what to read, what not to read",
+ *           §1.1, §3.2
  *
  *   A query at logical position t reads exactly the keys at logical positions
  *   max(0, t-W+1) .. t (W counts the current token) [M003 §03], [Ch10 §10.1];
