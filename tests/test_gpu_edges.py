@@ -242,3 +242,96 @@ def test_bwd_empty_sequence():
     for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
         assert torch.all(got[0] == 0), name
         check(got, ref, True, "bwd empty sequence " + name)
+
+
+@pytest.mark.parametrize("bias", [1.0, -1.0])
+def test_varlen_large_scores(bias):
+    """The packed layout through the reference-moving path."""
+    lens = [300, 0, 129, 77]
+    d, H, Hkv, W = 128, 4, 2, 96
+    total, mx = sum(lens), max(lens)
+    q, k, v = _qkv(1, H, Hkv, total, d, seed=97, qk_std=3.0, bias=bias, tdt=torch.bfloat16)
+    # token-major [total, heads, d]
+    q, k, v = (x[0].transpose(0, 1).contiguous() for x in (q, k, v))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    meta = swa.swa_blockmask_build(len(lens), mx, mx, W, 128, 64, q_len=np.array(lens),
+                                   k_len=np.array(lens))
+    md = swa.meta_to_device(meta, DEV)
+    o = torch.full((total, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    swa.swa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), o, W, md, torch.from_numpy(cu).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.fwd_varlen(f64(q), f64(k), f64(v), cu, W, 1 / math.sqrt(d))
+    check(o, ref, True, "varlen large scores bias=%g" % bias)
+
+
+@pytest.mark.parametrize("bias", [1.0, -1.0])
+def test_bwd_large_scores(bias):
+    """Gradients where the softmax is nearly one-hot (scaled scores ~ +-25
+    with a spread of +-5): P = exp(s - lse) from the forward's lse."""
+    q, k, v = _qkv(1, 4, 2, 300, 128, seed=98, qk_std=1.5, bias=bias, tdt=torch.bfloat16)
+    g = torch.Generator().manual_seed(99)
+    dout = (torch.randn(q.shape, generator=g) * 0.5).to(torch.bfloat16)
+    B, H, N, d = q.shape
+    W = 100
+    md = swa.meta_to_device(swa.swa_blockmask_build(B, N, N, W, 128, 64), DEV)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, dout))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    swa.swa_fwd(qd, kd, vd, o, W, md, lse=lse)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(swa.swa_bwd_workspace_size(B, H, N) // 4, dtype=torch.float32, device=DEV)
+    swa.swa_bwd(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, W, md)
+    torch.cuda.synchronize()
+    rq, rk, rv, rl = oracle.bwd(f64(q), f64(k), f64(v), f64(dout), W, 1 / math.sqrt(d))
+    # the forward's lse bar for bf16 (the row sum is taken over bf16-rounded P)
+    lerr = np.abs(f64(lse) - rl)
+    assert lerr.max() <= 4e-3, float(lerr.max())
+    for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        gg = f64(got)
+        scale = max(1.0, float(np.abs(ref).max()))
+        err = np.abs(gg - ref) / scale
+        assert np.all(np.isfinite(gg)), name
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (name, float(err.max()),
+                                                          float(err.mean()))
+
+
+@pytest.mark.parametrize("bias", [1.0, -1.0])
+def test_chunk_sinks_large_scores(bias):
+    """A chunk with 4 attention sinks (the sink segment of the key axis) and
+    scores far from the fixed reference."""
+    W, Tq, d, S = 128, 64, 128, 4
+    B, H, Hkv = 2, 8, 2
+    P = 300  # next position: the ring holds 172 .. 299, the sinks 0 .. 3
+    q, k, v = _qkv(B, H, Hkv, P + Tq, d, seed=100, qk_std=3.0, bias=bias, tdt=torch.bfloat16)
+    rs = np.array([P % W, P % W], dtype=np.int32)
+    kc = torch.empty(B, Hkv, W, d, dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    for s_ in range(W):  # slot s holds position P - W + ((s - rs) mod W)
+        pos = P - W + ((s_ - int(rs[0])) % W)
+        kc[:, :, s_], vc[:, :, s_] = k[:, :, pos], v[:, :, pos]
+    sk, sv = k[:, :, :S].contiguous(), v[:, :, :S].contiguous()
+    state = [None, None, rs, np.full(B, W, dtype=np.int32), np.full(B, P, dtype=np.int32)]
+    md = _chunk_meta_local(state, Tq, W, S)
+    qn, kn, vn = (x[:, :, P:].contiguous() for x in (q, k, v))
+    dev = [t.to(DEV).contiguous() for t in (qn, kn, vn, kc, vc, sk, sv)]
+    st = [torch.from_numpy(x.copy()).to(DEV) for x in state[2:]]
+    o = torch.full_like(dev[0], float("nan"))
+    swa.swa_prefill_chunk(dev[0], dev[1], dev[2], dev[3], dev[4], st[0], st[1], st[2], o, W, md,
+                          sink_k=dev[5], sink_v=dev[6])
+    torch.cuda.synchronize()
+    ref = oracle.chunk(f64(qn), f64(kn), f64(vn), f64(kc), f64(vc), rs, state[3], state[4], W,
+                       1 / math.sqrt(d), n_sink=S, sink_k=f64(sk), sink_v=f64(sv))
+    check(o, ref[0], True, "chunk sinks large scores bias=%g" % bias)
+    # the same rows of the full-sequence forward with sinks, positions P .. P+Tq-1
+    full = oracle.fwd_rows(f64(q), f64(k), f64(v), W, 1 / math.sqrt(d),
+                           [(b, h, P + i) for b in range(B) for h in range(H) for i in (0, 31, 63)],
+                           n_sink=S)
+    got = f64(o)[:, :, [0, 31, 63]].reshape(-1, d)
+    assert np.abs(got - full).max() <= 2e-2
+
+
+def _chunk_meta_local(state, Tq, W, S):
+    rs, cl, npos = state[2], state[3], state[4]
+    m = swa.swa_blockmask_build(len(npos), Tq, Tq, W, 128, 64, q_start=npos, k_start=npos,
+                                W_ring=W, ring_start=rs, cache_len=cl, next_pos=npos, n_sink=S)
+    return swa.meta_to_device(m, DEV)
