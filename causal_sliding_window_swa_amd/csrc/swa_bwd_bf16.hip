@@ -49,6 +49,21 @@ __device__ __forceinline__ int xcd_remap(int p, int T) {
     return x * q + (x < r ? x : r) + i;
 }
 
+// Workgroups go to the XCDs round-robin, about 64 per XCD at a time: in round
+// r XCD x runs the 64-item chunk 8r + (x + r) % 8 of the logical order, so the
+// items an XCD runs together are neighbours (shared tiles in its L2) and every
+// XCD draws from all parts of the order (even work when sequence lengths
+// differ).  The tail of T mod 512 items keeps contiguous ranges.  A bijection.
+__device__ __forceinline__ int xcd_deal(int p, int T) {
+    constexpr int C = 64;
+    const int Tm = T / (8 * C) * (8 * C);
+    if (p < Tm) {
+        const int x = p & 7, i = p >> 3, r = i / C, o = i % C;
+        return (r * 8 + ((x + r) & 7)) * C + o;
+    }
+    return Tm + xcd_remap(p - Tm, T - Tm);
+}
+
 // 16-byte chunk c of row r sits at physical chunk c ^ (r % chunks per row).
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
@@ -136,7 +151,7 @@ void dq_kernel(BwdArgs a) {
     const int lq = lane & 31, hh = lane >> 5;
     const int N = a.N;
     const int nqt = (N + 32 * NW - 1) / (32 * NW);
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = xcd_deal(blockIdx.x, gridDim.x);
     const int G = a.H / a.Hkv;
     const int h_in = L % G, qt = (L / G) % nqt, g = (L / (G * nqt)) % a.Hkv;
     const int b = L / (G * nqt * a.Hkv);
@@ -313,7 +328,7 @@ void dkdv_kernel(BwdArgs a) {
     const int lq = lane & 31, hh = lane >> 5;
     const int N = a.N, W = a.W;
     const int nkt = (N + BN - 1) / BN;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = xcd_deal(blockIdx.x, gridDim.x);
     const int kt = L % nkt, g = (L / nkt) % a.Hkv, b = L / (nkt * a.Hkv);
     const int G = a.H / a.Hkv;
     const int qlen = a.q_len ? a.q_len[b] : N;
