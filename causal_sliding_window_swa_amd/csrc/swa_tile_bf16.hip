@@ -423,7 +423,10 @@ void tile_kernel(AttnArgs a) {
         // (pk[kk] for 16-key step kk), and this tile's row sum of P
         bf16x8 pk[4];
         auto probs = [&]() -> float {
-            float acc = 0.f;
+            // one partial sum per 16-key step: four short dependency chains
+            // instead of one of 16, so that the row sum (and the rare-case
+            // check that waits for it) is ready sooner
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
             const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
@@ -438,10 +441,10 @@ void tile_kernel(AttnArgs a) {
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
                     const bf16x2 pr = {pk[kk][2 * t], pk[kk][2 * t + 1]};
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+                    acc[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc[kk], false);
                 }
             }
-            return half_swap_sum(acc);
+            return half_swap_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
         };
         __builtin_amdgcn_s_setprio(2);
         scores();
