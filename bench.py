@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -45,10 +46,16 @@ def parse():
 
 
 def src_digest(*names):
+    """sha256 prefix of the kernel sources with comments and whitespace
+    removed: the code the counters in profiles/hbm_traffic.json were taken
+    on (a comment edit keeps the record valid, a code edit voids it)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "causal_sliding_window_swa_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "causal_sliding_window_swa_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

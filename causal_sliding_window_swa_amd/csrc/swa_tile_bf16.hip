@@ -9,13 +9,14 @@
 // partial tiles are masked per element.
 //
 // Work split (tile_q = 32 * NW query rows, tile_k = 64 keys, head dim D):
-//   * one workgroup per (query tile, head, batch), ordered so that each XCD
-//     walks a contiguous range of (query tile, head) pairs with the query
-//     heads of one KV group next to each other: they read identical K/V tiles,
-//     and neighbouring query tiles share most of theirs, so both hit in that
-//     XCD's L2;
-//   * wave priority is raised over the MFMA sections, so that while one wave
-//     issues its matrix work the co-resident wave fills the VALU slots;
+//   * one workgroup per (query tile, head, batch).  In the logical order the
+//     query heads of one KV group are next to each other (they read identical
+//     K/V tiles) and then the query tiles (neighbours share most of theirs);
+//     chunks of 64 consecutive tiles are dealt to the XCDs so that the
+//     workgroups one XCD runs together hit in its L2 and every XCD gets an
+//     even share of the work (see xcd_deal);
+//   * wave priority is raised over the MFMA sections (measured neutral, kept
+//     as the intent: one wave issues matrix work while the other fills VALU);
 //   * K and V tiles go straight from HBM to LDS (buffer_load_dwordx4 ... lds,
 //     no register staging), double-buffered: the next tile streams in while
 //     this one is computed; rows are XOR-swizzled in 16-byte chunks so that
