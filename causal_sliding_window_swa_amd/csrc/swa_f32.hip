@@ -13,12 +13,14 @@
 namespace swa {
 namespace {
 
-// One query row: fold key (pos, krow, vrow) into the running state.
+// One query row: fold key (pos, krow, vrow) into the running state.  The
+// methods are inlined at every call site: called out of line (the chunk and
+// decode kernels call add from two places), the state went through scratch.
 template <int DMAX>
 struct RowState {
     float q[DMAX], o[DMAX];
     float m, l;
-    __device__ void init(const float *qrow, int d) {
+    __device__ __forceinline__ void init(const float *qrow, int d) {
 #pragma unroll
         for (int c = 0; c < DMAX; c++) {
             q[c] = (c < d) ? qrow[c] : 0.f;
@@ -27,7 +29,7 @@ struct RowState {
         m = -INFINITY;
         l = 0.f;
     }
-    __device__ void add(const float *krow, const float *vrow, int d, float scale) {
+    __device__ __forceinline__ void add(const float *krow, const float *vrow, int d, float scale) {
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < DMAX; c++)
@@ -42,8 +44,8 @@ struct RowState {
             if (c < d) o[c] = fmaf(p, vrow[c], o[c] * corr);
         m = m2;
     }
-    __device__ float lse() const { return (l > 0.f) ? m + logf(l) : -INFINITY; }
-    __device__ void store(float *orow, int d) const {
+    __device__ __forceinline__ float lse() const { return (l > 0.f) ? m + logf(l) : -INFINITY; }
+    __device__ __forceinline__ void store(float *orow, int d) const {
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
         for (int c = 0; c < DMAX; c++)
