@@ -172,8 +172,8 @@ void tile_kernel(AttnArgs a) {
         }
     }
 
-    // ---- key/value rows of a tile (rows past the data are clamped to a real
-    // row: they are always masked, and their values stay finite)
+    // ---- key/value rows of a tile (rows past the data read as zeros through
+    // the buffer range check below: finite, and always masked)
     const size_t kvh = (size_t)b * a.Hkv + g;
     // global row stride in bytes: D*2, or Hkv*D*2 in the packed layout
     const int RSB = PK ? a.Hkv * ROWB : ROWB;
