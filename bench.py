@@ -385,6 +385,23 @@ def main():
                "sample": "the whole prefill workload (B=1, H=32, N=8192, W=512, d=128) "
                          "in fp64, %d passes, %.1f s" % (reps, sec)}
         log("oracle: %d passes in %.2f s" % (reps, sec))
+        # the same at one thread, on 2 of the 32 heads
+        nthr = oracle.num_threads()
+        oracle.set_num_threads(1)
+        q2, k2, v2 = (x[:, :2].copy() for x in (qs, ks, vs))
+        reps1, sec1 = 0, 0.0
+        while sec1 < 5.0 and reps1 < 20:
+            t0 = time.perf_counter()
+            oracle.fwd(q2, k2, v2, 512, 1 / math.sqrt(128))
+            sec1 += time.perf_counter() - t0
+            reps1 += 1
+        oracle.set_num_threads(nthr)
+        cpu["single_thread"] = {
+            "value": round(4.0 * 128 * meta["valid_pairs"] * 2 * reps1 / sec1 / 1e12, 6),
+            "unit": "TFLOP/s", "cores": 1,
+            "sample": "2 of the 32 heads of the prefill workload in fp64, %d passes, %.1f s"
+                      % (reps1, sec1)}
+        log("oracle, one thread: %d passes in %.2f s" % (reps1, sec1))
 
     pf = out["prefill"]
     value = pf["flops"] / (pf["wall_ms"] * 1e-3) / 1e12

@@ -91,11 +91,17 @@ class Oracle:
         lib.orc_cache_bytes_layers.restype = L
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_set_num_threads.argtypes = [i]
+        lib.orc_set_num_threads.restype = None
         self.lib = lib
         self.path = lib_path
 
     def num_threads(self) -> int:
         return self.lib.orc_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        """Thread count of later calls (for timing at one thread)."""
+        self.lib.orc_set_num_threads(int(n))
 
     def fwd(self, q, k, v, W: int, scale: float, q_len=None, n_sink: int = 0) -> np.ndarray:
         """Full-sequence SWA forward.  q [B,H,N,d], k/v [B,Hkv,N,d] -> o [B,H,N,d];
@@ -270,6 +276,10 @@ def default() -> Oracle:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
 
 
 def fwd(*a, **kw):

@@ -589,6 +589,16 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Sets the thread count of later calls (timing at one thread); n < 1 is 1. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Gradients of the full-sequence forward, for a scalar loss whose gradient
  * with respect to the output o is dout.  [M003 §07] asks that the Q/K/V
