@@ -13,6 +13,7 @@ Functions keep the ABI's names:
     swa_fwd_varlen(q, k, v, o, W, meta, cu_seqlens, lse=None, scale=None)
     swa_bwd_workspace_size(B, H, N)
     swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, scale=None)
+    swa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, cu_seqlens, scale=None)
     swa_prefill_chunk(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len,
                       next_pos, o, W, meta, tile_q, tile_k, scale=None)
     swa_decode_workspace_size(B, H, d, W)
@@ -44,7 +45,8 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 # Symbols declared in include/swa.h (checked by the CPU tests).
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
            "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
-           "swa_fwd_varlen", "swa_layer_plan", "swa_cache_bytes", "swa_last_error")
+           "swa_fwd_varlen", "swa_bwd_varlen", "swa_layer_plan", "swa_cache_bytes",
+           "swa_last_error")
 
 
 class SwaError(RuntimeError):
@@ -82,6 +84,7 @@ def lib():
             L.swa_bwd_workspace_size.restype = ctypes.c_size_t
             L.swa_bwd.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
                                   P, P, ctypes.c_size_t, F, P]
+            L.swa_bwd_varlen.argtypes = [I] * 11 + [P] * 14 + [ctypes.c_size_t, F, P]
             L.swa_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, P, P, I, I, P, P, P, P, P, P,
                                             P, P, P, P, P, P, F, P]
             L.swa_decode_workspace_size.argtypes = [I, I, I, I]
@@ -94,6 +97,7 @@ def lib():
             L.swa_last_error.restype = ctypes.c_char_p
             for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
                       "swa_prefill_chunk", "swa_decode", "swa_bwd", "swa_fwd_varlen",
+                      "swa_bwd_varlen",
                       "swa_layer_plan", "swa_cache_bytes"):
                 getattr(L, n).restype = ctypes.c_int
             _lib = L
@@ -327,6 +331,41 @@ def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, s
                          _dptr(q_len), _dptr(meta["row_ptr"]), _dptr(meta["col"]),
                          _dptr(meta["cls"]), _dptr(dq), _dptr(dk), _dptr(dv), _dptr(workspace),
                          ctypes.c_size_t(ws_bytes), ctypes.c_float(scale), _stream(q, stream)))
+    return dq, dk, dv
+
+
+def swa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, cu_seqlens,
+                   scale=None, stream=None):
+    """Gradients of swa_fwd_varlen (bf16).  q,o,dout,dq [total,H,d]; k,v,dk,dv
+    [total,Hkv,d] token-major; lse fp32 [total,H] from swa_fwd_varlen; meta and
+    cu_seqlens as for swa_fwd_varlen; workspace: device tensor of at least
+    swa_bwd_workspace_size(1, H, total) bytes."""
+    for t in (q, k, v, o, dout, lse, dq, dk, dv):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (total, Hkv, d) and tuple(v.shape) == (total, Hkv, d) and
+             tuple(o.shape) == (total, H, d) and tuple(dout.shape) == (total, H, d) and
+             tuple(dq.shape) == (total, H, d) and tuple(dk.shape) == (total, Hkv, d) and
+             tuple(dv.shape) == (total, Hkv, d) and tuple(lse.shape) == (total, H),
+             "shape mismatch")
+    _require(len({t.dtype for t in (q, k, v, o, dout, dq, dk, dv)}) == 1, "dtype mismatch")
+    B = cu_seqlens.numel() - 1
+    _check_meta(meta, "swa_bwd_varlen", B=B, W=W, W_ring=0)
+    _require(meta["nk_lin"] == meta["nq"], "swa_bwd_varlen: metadata must be built with "
+             "nq = nk_lin = max_len")
+    n = meta["max_len"]
+    _require(meta["cls"].numel() == B * (-(-n // meta["tile_q"])) * (-(-n // meta["tile_k"])),
+             "swa_bwd_varlen: class grid size does not match the call")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().swa_bwd_varlen(_dtype_code(q), B, H, Hkv, total, n, d, W,
+                                meta.get("n_sink", 0), meta["tile_q"], meta["tile_k"],
+                                _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(dout), _dptr(lse),
+                                _dptr(cu_seqlens), _dptr(meta["row_ptr"]), _dptr(meta["col"]),
+                                _dptr(meta["cls"]), _dptr(dq), _dptr(dk), _dptr(dv),
+                                _dptr(workspace), ctypes.c_size_t(ws_bytes),
+                                ctypes.c_float(scale), _stream(q, stream)))
     return dq, dk, dv
 
 

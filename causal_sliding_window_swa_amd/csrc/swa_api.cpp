@@ -188,6 +188,7 @@ extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     if (tile_q < 1 || tile_k < 1)
         return fail(SWA_EINVAL, "%s: tiles must be positive (tile_q=%d tile_k=%d)", fn, tile_q,
                     tile_k);
+    if ((rc = check_span(fn, dt, N, 2LL * d))) return rc;
     const void *ptrs[] = {q, k, v, o, dout, lse_dev, dq, dk, dv, workspace, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace",
                            "row_ptr", "col"};
@@ -210,6 +211,54 @@ extern "C" int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     a.n_sink = n_sink;
     a.scale = scale;
     a.bf16 = dt == SWA_BF16;
+    return launched(fn, swa::launch_bwd(a, (hipStream_t)stream));
+}
+
+extern "C" int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len,
+                              int d, int W, int n_sink, int tile_q, int tile_k, const void *q,
+                              const void *k, const void *v, const void *o, const void *dout,
+                              const float *lse_dev, const int32_t *cu_seqlens_dev,
+                              const int32_t *row_ptr_dev, const int32_t *col_dev,
+                              const uint8_t *cls_dev, void *dq, void *dk, void *dv,
+                              void *workspace, size_t ws_bytes, float scale, void *stream) {
+    static const char *fn = "swa_bwd_varlen";
+    swa::clear_error();
+    int rc;
+    if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
+    if (total < 1 || max_len < 1 || max_len > total)
+        return fail(SWA_EINVAL, "%s: need 1 <= max_len <= total (total=%d max_len=%d)", fn,
+                    total, max_len);
+    if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
+    if ((rc = check_dtype_d(fn, dt, d))) return rc;
+    if (dt != SWA_BF16)
+        return fail(SWA_EUNSUPPORTED, "%s: the packed backward is bf16 only", fn);
+    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    // query-side rows are H * d elements apart (the wider of the two strides)
+    if ((rc = check_span(fn, dt, max_len, 2LL * d * H))) return rc;
+    const void *ptrs[] = {q, k, v, o, dout, lse_dev, dq, dk, dv, workspace, row_ptr_dev, col_dev};
+    const char *names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace",
+                           "row_ptr", "col"};
+    if ((rc = check_ptrs(fn, ptrs, names, 12))) return rc;
+    if (!cls_dev || !cu_seqlens_dev)
+        return fail(SWA_EINVAL, "%s: cls and cu_seqlens are required", fn);
+    if (ws_bytes < swa_bwd_workspace_size(1, H, total))
+        return fail(SWA_EINVAL, "%s: workspace of %zu bytes is below the %zu required", fn,
+                    ws_bytes, swa_bwd_workspace_size(1, H, total));
+    if (!(scale > 0.f) || scale == INFINITY)
+        return fail(SWA_EINVAL, "%s: scale must be positive and finite", fn);
+
+    swa::BwdArgs a = {};
+    a.B = B; a.H = H; a.Hkv = Hkv; a.N = max_len; a.d = d; a.W = W;
+    a.tile_q = tile_q; a.tile_k = tile_k;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse_dev;
+    a.cu = cu_seqlens_dev;
+    a.row_ptr = row_ptr_dev; a.col = col_dev; a.cls = cls_dev;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dvec = (float *)workspace;
+    a.n_sink = n_sink;
+    a.scale = scale;
+    a.bf16 = 1;
     return launched(fn, swa::launch_bwd(a, (hipStream_t)stream));
 }
 

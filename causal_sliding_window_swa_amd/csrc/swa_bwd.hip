@@ -211,6 +211,8 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
+    // a packed batch runs on the bf16 MFMA kernels only
+    if (a.cu) return bwd_bf16_supported(a) ? launch_bwd_bf16(a, s) : hipErrorNotSupported;
     if (!a.bf16) return launch_t<float>(a, s);
     if (!bwd_bf16_supported(a)) return launch_t<__bf16>(a, s);
     // the MFMA dq kernel computes the row values D itself

@@ -21,6 +21,12 @@
 // block: S = Q K^T and dP = dO V^T (A = Q or dO rows from LDS, B = the wave's
 // K or V rows), P and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T
 // and Q^T read by transposing LDS reads.  Each lane holds one key column.
+//
+// PK (packed batch): the same kernels over token-major tensors, sequence b
+// being tokens cu[b] .. cu[b+1]-1; rows are then H*D (Q side) or Hkv*D (K
+// side) elements apart and lse / D are [tokens][H].  The grid is sized by
+// the longest sequence; work items past a sequence's end find empty metadata
+// rows and write nothing, and no row past it is read or written.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -106,40 +112,43 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define SWA_RSRC(base, bytes) \
     __builtin_amdgcn_make_buffer_rsrc((void *)(base), 0, (bytes), 0x00020000)
 
-// Copy 64 rows x D of a row-major bf16 matrix of nrows rows (rows row0..;
-// rows past the data read as zeros: finite, and masked) into an LDS tile,
-// swizzled; NW waves share the work.  The buffer (MUBUF) form of the LDS DMA
+// Copy 64 rows x D of a bf16 matrix of nrows rows, rsb bytes apart (rows
+// row0..; rows past the data read as zeros: finite, and masked) into an LDS
+// tile, swizzled; NW waves share the work.  The buffer (MUBUF) form of the LDS DMA
 // keeps the compiler's LDS-read waits partial (the FLAT global_load_lds form
 // makes every wait lgkmcnt(0)).
 template <int D, int NW>
-__device__ __forceinline__ void stage_rows(const __bf16 *src, int row0, int nrows, char *dst,
-                                           int wave, int lane) {
+__device__ __forceinline__ void stage_rows(const __bf16 *src, int row0, int nrows, int rsb,
+                                           char *dst, int wave, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist for the device only
     constexpr int ROWB = D * 2, CPR = D / 8, RPL = 64 / CPR, LPW = BN / RPL / NW;
-    const auto rs = SWA_RSRC(src, nrows * ROWB);
+    // the range ends with the last row's own bytes: a row past it starts at or
+    // beyond the end and reads as zeros
+    const auto rs = SWA_RSRC(src, nrows > 0 ? (nrows - 1) * rsb + ROWB : 0);
 #pragma unroll
     for (int i = 0; i < LPW; i++) {
         const int ins = wave * LPW + i;
         const int r = ins * RPL + lane / CPR;
         const int pch = lane % CPR;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + ins * 1024), 16,
-                                                 (row0 + r) * ROWB + (pch ^ swz<CPR>(r)) * 16, 0,
+                                                 (row0 + r) * rsb + (pch ^ swz<CPR>(r)) * 16, 0,
                                                  0, 0);
     }
 #endif
 }
 
-// One fp32 value per lane (index i of an n-element array; zero past the end)
-// into 64 consecutive LDS words.
-__device__ __forceinline__ void stage_vals(const float *src, int i, int n, char *dst) {
+// One fp32 value per lane (element i of an n-element array whose elements
+// are `stride` floats apart; zero past the end) into 64 consecutive LDS words.
+__device__ __forceinline__ void stage_vals(const float *src, int i, int n, int stride,
+                                           char *dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(SWA_RSRC(src, n * 4), (lds_void *)dst, 4, i * 4, 0,
-                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(SWA_RSRC(src, n > 0 ? ((n - 1) * stride + 1) * 4 : 0),
+                                             (lds_void *)dst, 4, i * stride * 4, 0, 0, 0);
 #endif
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel(BwdArgs a) {
     constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
@@ -156,11 +165,15 @@ void dq_kernel(BwdArgs a) {
     const int h_in = L % G, qt = (L / G) % nqt, g = (L / (G * nqt)) % a.Hkv;
     const int b = L / (G * nqt * a.Hkv);
     const int h = g * G + h_in;
-    const int qlen = a.q_len ? a.q_len[b] : N;
+    // rows of this request that exist (all N when padded)
+    const int cub = PK ? a.cu[b] : 0;
+    const int nrows = PK ? a.cu[b + 1] - cub : N;
+    const int qlen = PK ? nrows : (a.q_len ? a.q_len[b] : N);
 
     const int myrow = qt * 32 * NW + wave * 32 + lq;
     const bool qvalid = myrow < qlen;
-    const size_t rowidx = ((size_t)b * a.H + h) * N + myrow;
+    // index of this row in the [.][H][N] (or [tokens][H]) row arrays
+    const size_t rowidx = PK ? (size_t)(cub + myrow) * a.H + h : ((size_t)b * a.H + h) * N + myrow;
     bf16x8 qf[KS], dof[KS];
     {
         const __bf16 *qp = (const __bf16 *)a.q + rowidx * D;
@@ -168,8 +181,8 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             const u32x4 z = {0, 0, 0, 0};
-            qf[ks] = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(qp + ks * 16 + hh * 8) : z);
-            dof[ks] = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(dp + ks * 16 + hh * 8) : z);
+            qf[ks] = __builtin_bit_cast(bf16x8, (myrow < nrows) ? ld16(qp + ks * 16 + hh * 8) : z);
+            dof[ks] = __builtin_bit_cast(bf16x8, (myrow < nrows) ? ld16(dp + ks * 16 + hh * 8) : z);
         }
     }
     // D = <dO, O> of this row: each lane of the pair (l, l^32) holds half of
@@ -181,25 +194,27 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             const u32x4 z = {0, 0, 0, 0};
-            const bf16x8 of = __builtin_bit_cast(bf16x8, (myrow < N) ? ld16(op + ks * 16 + hh * 8) : z);
+            const bf16x8 of =
+                __builtin_bit_cast(bf16x8, (myrow < nrows) ? ld16(op + ks * 16 + hh * 8) : z);
 #pragma unroll
             for (int t = 0; t < 8; t++) acc = fmaf((float)of[t], (float)dof[ks][t], acc);
         }
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
                                                         false, false);
         Dr = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        if (myrow < N && hh == 0) a.dvec[rowidx] = Dr;
+        if (myrow < nrows && hh == 0) a.dvec[rowidx] = Dr;
         if (!qvalid) Dr = 0.f;
     }
     const float c2 = a.scale * LOG2E;
     const float lse2 = qvalid ? a.lse[rowidx] * LOG2E : 0.f;
 
-    const size_t kvh = (size_t)b * a.Hkv + g;
-    const __bf16 *kb = (const __bf16 *)a.k + kvh * (size_t)N * D;
-    const __bf16 *vb = (const __bf16 *)a.v + kvh * (size_t)N * D;
+    const size_t kvo = PK ? ((size_t)cub * a.Hkv + g) * D : ((size_t)b * a.Hkv + g) * N * D;
+    const __bf16 *kb = (const __bf16 *)a.k + kvo;
+    const __bf16 *vb = (const __bf16 *)a.v + kvo;
+    const int krsb = PK ? a.Hkv * ROWB : ROWB;  // bytes between key rows
     auto issue = [&](int kt, char *dst) __attribute__((always_inline)) {
-        stage_rows<D, NW>(kb, kt * BN, N, dst, wave, lane);
-        stage_rows<D, NW>(vb, kt * BN, N, dst + TILEB, wave, lane);
+        stage_rows<D, NW>(kb, kt * BN, nrows, krsb, dst, wave, lane);
+        stage_rows<D, NW>(vb, kt * BN, nrows, krsb, dst + TILEB, wave, lane);
     };
 
     f32x16 dqacc[DB];
@@ -300,7 +315,7 @@ void dq_kernel(BwdArgs a) {
         if (e + 1 < e1) tile(e + 1, stage1, stage0);
     }
 
-    if (myrow < N) {
+    if (myrow < nrows) {
         __bf16 *op = (__bf16 *)a.dq + rowidx * D;
 #pragma unroll
         for (int db = 0; db < DB; db++)
@@ -315,7 +330,7 @@ void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PK>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
 void dkdv_kernel(BwdArgs a) {
     constexpr int NW = 2, KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
@@ -331,13 +346,17 @@ void dkdv_kernel(BwdArgs a) {
     const int L = xcd_deal(blockIdx.x, gridDim.x);
     const int kt = L % nkt, g = (L / nkt) % a.Hkv, b = L / (nkt * a.Hkv);
     const int G = a.H / a.Hkv;
-    const int qlen = a.q_len ? a.q_len[b] : N;
+    // rows (and keys) of this request that exist (all N when padded)
+    const int cub = PK ? a.cu[b] : 0;
+    const int nrows = PK ? a.cu[b + 1] - cub : N;
+    const int qlen = PK ? nrows : (a.q_len ? a.q_len[b] : N);
     const int tq = a.tile_q;
     const int nqt = (N + tq - 1) / tq;
 
     const int mykey = kt * BN + wave * 32 + lq;
-    const size_t kvh = (size_t)b * a.Hkv + g;
-    const size_t keyidx = kvh * N + mykey;
+    // index of this key in the [.][Hkv][N] (or [tokens][Hkv]) row arrays
+    const size_t keyidx =
+        PK ? (size_t)(cub + mykey) * a.Hkv + g : ((size_t)b * a.Hkv + g) * N + mykey;
     bf16x8 kf[KS], vf[KS];
     {
         const __bf16 *kp = (const __bf16 *)a.k + keyidx * D;
@@ -345,8 +364,8 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             const u32x4 z = {0, 0, 0, 0};
-            kf[ks] = __builtin_bit_cast(bf16x8, (mykey < N) ? ld16(kp + ks * 16 + hh * 8) : z);
-            vf[ks] = __builtin_bit_cast(bf16x8, (mykey < N) ? ld16(vp + ks * 16 + hh * 8) : z);
+            kf[ks] = __builtin_bit_cast(bf16x8, (mykey < nrows) ? ld16(kp + ks * 16 + hh * 8) : z);
+            vf[ks] = __builtin_bit_cast(bf16x8, (mykey < nrows) ? ld16(vp + ks * 16 + hh * 8) : z);
         }
     }
     // visible query rows of this lane's key: [ka, kb_] (every later row for an
@@ -394,7 +413,7 @@ void dkdv_kernel(BwdArgs a) {
     auto live_from = [&](int t) __attribute__((always_inline)) -> int  {
         for (; t < nsteps; t++) {
             const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
-            if (cls_of(qt) != 0 && qt * tq + sub * BN < N) break;
+            if (cls_of(qt) != 0 && qt * tq + sub * BN < nrows) break;
         }
         return t;
     };
@@ -404,18 +423,21 @@ void dkdv_kernel(BwdArgs a) {
         s0 = qt * tq + sub * BN;
         // a full class counts only in-range pairs: steps or key tiles cut by
         // the array edge are masked too
-        part = cls_of(qt) == 2 || s0 + BN > N || kt * BN + BN > N;
+        part = cls_of(qt) == 2 || s0 + BN > nrows || kt * BN + BN > nrows;
     };
     auto issue = [&](int t, char *dst) __attribute__((always_inline)) {
         int hq, s0;
         bool part;
         step_rows(t, hq, s0, part);
-        const size_t rb = ((size_t)b * a.H + hq) * N;
-        stage_rows<D, NW>((const __bf16 *)a.q + rb * D, s0, N, dst, wave, lane);
-        stage_rows<D, NW>((const __bf16 *)a.dout + rb * D, s0, N, dst + TILEB, wave, lane);
+        // row 0 of head hq in the row arrays; rows are H apart when packed
+        const size_t rb = PK ? (size_t)cub * a.H + hq : ((size_t)b * a.H + hq) * N;
+        const int rst = PK ? a.H : 1;
+        stage_rows<D, NW>((const __bf16 *)a.q + rb * D, s0, nrows, rst * ROWB, dst, wave, lane);
+        stage_rows<D, NW>((const __bf16 *)a.dout + rb * D, s0, nrows, rst * ROWB, dst + TILEB,
+                          wave, lane);
         // row values of the 64 rows (zeros past the data, which is masked)
         const float *src = (wave == 0) ? (a.lse + rb) : (a.dvec + rb);
-        stage_vals(src, s0 + lane, N, dst + 2 * TILEB + wave * 256);
+        stage_vals(src, s0 + lane, nrows, rst, dst + 2 * TILEB + wave * 256);
     };
 
     const int tr_j = lane & 15;
@@ -501,7 +523,7 @@ void dkdv_kernel(BwdArgs a) {
         t = t2;
     }
 
-    if (mykey < N) {
+    if (mykey < nrows) {
         __bf16 *kp = (__bf16 *)a.dk + keyidx * D;
         __bf16 *vp = (__bf16 *)a.dv + keyidx * D;
 #pragma unroll
@@ -520,7 +542,7 @@ void dkdv_kernel(BwdArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool PK>
 hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
     hipError_t e;
     const int NWq = a.tile_q == 128 ? 4 : 2;
@@ -529,11 +551,11 @@ hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
     const long gq = nqt * a.H * a.B, gk = nkt * a.Hkv * a.B;
     if (gq > 0x7fffffffL || gk > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (NWq == 4)
-        hipLaunchKernelGGL((dq_kernel<D, 4>), dim3((unsigned)gq), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((dq_kernel<D, 4, PK>), dim3((unsigned)gq), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)gq), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((dq_kernel<D, 2, PK>), dim3((unsigned)gq), dim3(128), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)gk), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, PK>), dim3((unsigned)gk), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 
@@ -545,7 +567,8 @@ bool bwd_bf16_supported(const BwdArgs &a) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
-    return a.d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+    if (a.cu) return a.d == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
+    return a.d == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 
 }  // namespace swa

@@ -81,9 +81,14 @@ struct BwdArgs {
     int n_sink;
     float scale;
     int bf16;
+    // may be null: packed batch, sequence b = tokens cu[b] .. cu[b+1]-1 of
+    // token-major q, o, dout, dq [tokens][H][d], k, v, dk, dv [tokens][Hkv][d],
+    // lse and dvec [tokens][H]; N is then the longest sequence
+    const int32_t *cu;
 };
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
-// bf16 MFMA kernels (swa_bwd_bf16.hip): d in {64, 128}, tile_k 64, tile_q in {64, 128}.
+// bf16 MFMA kernels (swa_bwd_bf16.hip): d in {64, 128}, tile_k 64, tile_q in {64, 128};
+// the only kernels that take a packed batch.
 bool bwd_bf16_supported(const BwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 

@@ -194,6 +194,31 @@ int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
             void *dq, void *dk, void *dv, void *workspace, size_t ws_bytes,
             float scale, void *stream);
 
+/* Gradients of swa_fwd_varlen: the quantities of swa_bwd for a packed
+ * variable-length batch [M003 §07 for the gradients; Blog §3.3 and §5.2 for
+ * the packed layout with per-sequence windows].  Sequence b owns tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 (token i of it at logical position i,
+ * positions below n_sink are its attention sinks).  Layout is token-major:
+ * q, o, dout, dq [total][H][d]; k, v, dk, dv [total][Hkv][d]; lse_dev the
+ * fp32 [total][H] that swa_fwd_varlen wrote for this q, k, v and n_sink.
+ * Metadata: that of swa_fwd_varlen (nq = nk_lin = max_len, q_len = k_len =
+ * the lengths), with cls_dev its class grid [B][nqt][nkt].  workspace: fp32
+ * row values [total][H], ws_bytes >= swa_bwd_workspace_size(1, H, total).
+ * Every output row is written; no padding is read or written.  The kernels
+ * do not re-check cu_seqlens against the metadata: inconsistent ones are a
+ * caller error.
+ * Supported: dt = SWA_BF16, d in {64, 128}, (tile_q, tile_k) = (128, 64) or
+ * (64, 64), max_len * H * d * 2 < 2^31; anything else is SWA_EUNSUPPORTED.
+ * Errors: SWA_EINVAL (as swa_fwd_varlen, NULL cls_dev, small workspace),
+ * SWA_EUNSUPPORTED, SWA_EHIP. */
+int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len, int d, int W,
+                   int n_sink, int tile_q, int tile_k,
+                   const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse_dev, const int32_t *cu_seqlens_dev,
+                   const int32_t *row_ptr_dev, const int32_t *col_dev, const uint8_t *cls_dev,
+                   void *dq, void *dk, void *dv, void *workspace, size_t ws_bytes,
+                   float scale, void *stream);
+
 /* Chunked prefill of Tq new tokens against a ring-buffer cache [Ch10 §10.2],
  * [Blog §3.2], [M003 §06].
  * q, o [B][H][Tq][d]; k_new, v_new [B][Hkv][Tq][d]; k_cache, v_cache

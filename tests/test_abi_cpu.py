@@ -116,6 +116,40 @@ def test_varlen_validation_codes():
     assert _varlen(d=96) == swa.SWA_EUNSUPPORTED
 
 
+def _bwd_varlen(dt=0, total=100, max_len=60, d=128, W=16, tq=128, tk=64, cu=True, cls=True,
+                ws=None, H=4, n_sink=0):
+    p = ctypes.c_void_p(16)
+    if ws is None:
+        ws = swa.swa_bwd_workspace_size(1, H, total)
+    return swa.lib().swa_bwd_varlen(dt, 2, H, 2, total, max_len, d, W, n_sink, tq, tk,
+                                    p, p, p, p, p, p, p if cu else None, p, p,
+                                    p if cls else None, p, p, p, p, ctypes.c_size_t(ws),
+                                    ctypes.c_float(0.1), None)
+
+
+def test_bwd_varlen_validation_codes():
+    """Every refusal happens before a launch (the pointers are never touched)."""
+    assert _bwd_varlen(total=0) == swa.SWA_EINVAL
+    assert _bwd_varlen(max_len=0) == swa.SWA_EINVAL
+    assert _bwd_varlen(max_len=101) == swa.SWA_EINVAL
+    assert _bwd_varlen(W=0) == swa.SWA_EINVAL
+    assert _bwd_varlen(n_sink=-1) == swa.SWA_EINVAL
+    assert _bwd_varlen(cu=False) == swa.SWA_EINVAL
+    assert _bwd_varlen(cls=False) == swa.SWA_EINVAL
+    # the packed backward runs on the bf16 MFMA kernels only
+    assert _bwd_varlen(dt=1) == swa.SWA_EUNSUPPORTED
+    assert "bf16" in swa.swa_last_error()
+    assert _bwd_varlen(d=96) == swa.SWA_EUNSUPPORTED
+    assert _bwd_varlen(tq=32) == swa.SWA_EUNSUPPORTED
+    assert _bwd_varlen(tk=128) == swa.SWA_EUNSUPPORTED
+    # workspace: fp32 row values [total][H]
+    assert _bwd_varlen(ws=100 * 4 * 4 - 1) == swa.SWA_EINVAL
+    assert "workspace" in swa.swa_last_error()
+    # query rows H * d * 2 bytes apart: max_len = 2^20, H = 8, d = 128 spans 2^31
+    assert _bwd_varlen(total=1 << 20, max_len=1 << 20, H=8) == swa.SWA_EUNSUPPORTED
+    assert "span" in swa.swa_last_error()
+
+
 def _chunk(Tq=64, W=128, tk=64, d=128, nullstate=False, sink=0, sink_ptr=16):
     p = ctypes.c_void_p(16)
     st = None if nullstate else p
@@ -216,6 +250,15 @@ def test_binding_rejects_mismatched_metadata():
     kv = torch.zeros(100, 2, 128, dtype=bf)
     with pytest.raises(swa.SwaError, match="B=3"):
         swa.swa_fwd_varlen(t, kv, kv.clone(), t.clone(), 16, mv, cu)
+    wsv = torch.zeros(100 * 4)
+    with pytest.raises(swa.SwaError, match="B=3"):
+        swa.swa_bwd_varlen(t, kv, kv.clone(), t.clone(), t.clone(), torch.zeros(100, 4),
+                           t.clone(), kv.clone(), kv.clone(), wsv, 16, mv, cu)
+    # packed backward with a build for a padded (nq != nk_lin) shape
+    mp = swa.meta_to_device(swa.swa_blockmask_build(2, 60, 64, 16, 128, 64), "cpu")
+    with pytest.raises(swa.SwaError, match="nq = nk_lin"):
+        swa.swa_bwd_varlen(t, kv, kv.clone(), t.clone(), t.clone(), torch.zeros(100, 4),
+                           t.clone(), kv.clone(), kv.clone(), wsv, 16, mp, cu)
     # a hand-made dict without the build's shape is refused too
     bad = {x: meta[x] for x in ("row_ptr", "col", "col_cls", "cls", "tile_q", "tile_k")}
     with pytest.raises(swa.SwaError, match="lacks"):

@@ -103,3 +103,63 @@ def test_varlen_gqa_workload_sampled():
                           rows, q_len=np.array(lens, dtype=np.int32))
     got = np.stack([f64(o[cu[b] + i, h]) for b, h, i in rows])
     check(got, ref, True, "varlen GQA workload sampled")
+
+
+def run_bwd_varlen(lens, H, Hkv, d, W, S, tq, seed):
+    """Packed forward then packed backward on the GPU; returns the packed
+    gradients and the padded fp64 inputs they came from."""
+    B, N = len(lens), max(lens)
+    inp = synth.gen_bwd(B, H, Hkv, N, d, seed=seed)
+    pack = lambda x: torch.cat([x[b, :, :L].transpose(0, 1) for b, L in enumerate(lens)]
+                               ).contiguous()
+    q, k, v, do = (pack(inp[n]).to(DEV) for n in ("q", "k", "v", "dout"))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    meta = swa.swa_blockmask_build(B, N, N, W, tq, 64, q_len=lens, k_len=lens, n_sink=S)
+    md = swa.meta_to_device(meta, DEV)
+    total = q.shape[0]
+    o = torch.empty_like(q)
+    lse = torch.full((total, H), float("nan"), device=DEV)
+    swa.swa_fwd_varlen(q, k, v, o, W, md, cu, lse=lse)
+    # NaN-filled outputs: every packed row must be written
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    ws = torch.empty(swa.swa_bwd_workspace_size(1, H, total) // 4, device=DEV)
+    swa.swa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, W, md, cu)
+    torch.cuda.synchronize()
+    return dq, dk, dv, inp
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tq", [128, 64])
+@pytest.mark.parametrize("W,S", [(1, 0), (17, 0), (100, 4), (400, 0)])
+def test_bwd_varlen_bf16(d, tq, W, S):
+    """Packed backward against the oracle's padded backward of the same
+    sequences, mapped to packed order (grouped heads, H=4 over Hkv=2)."""
+    lens = [333, 1, 64, 200, 129]
+    dq, dk, dv, inp = run_bwd_varlen(lens, 4, 2, d, W, S, tq, seed=900 + W + d)
+    L = np.array(lens, dtype=np.int32)
+    rq, rk, rv, _ = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"]),
+                               W, 1 / math.sqrt(d), q_len=L, n_sink=S)
+    packed = lambda r: np.concatenate([r[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    where = "bwd varlen d=%d tq=%d W=%d S=%d" % (d, tq, W, S)
+    for got, ref, nm in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        ref = packed(ref)
+        got = f64(got)
+        assert np.all(np.isfinite(got)), "unwritten or non-finite rows, " + where + " " + nm
+        err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (where, nm, float(err.max()))
+
+
+def test_bwd_varlen_empty_sequences_mha():
+    """Zero-length sequences among the packed ones (one head per group)."""
+    lens = [0, 97, 1, 0, 190]
+    dq, dk, dv, inp = run_bwd_varlen(lens, 2, 2, 128, 64, 0, 128, seed=955)
+    L = np.array(lens, dtype=np.int32)
+    rq, rk, rv, _ = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"]),
+                               64, 1 / math.sqrt(128), q_len=L)
+    packed = lambda r: np.concatenate([r[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    for got, ref, nm in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        ref = packed(ref)
+        got = f64(got)
+        assert got.shape == ref.shape and np.all(np.isfinite(got)), nm
+        err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (nm, float(err.max()))
