@@ -285,6 +285,22 @@ def main():
         out["gqa_packed"] = dict(wall_ms=w3p, kernel_ms=e3p, flops=out["gqa"]["flops"],
                                  tokens=int(sum(lens)))
         log("gqa packed: wall %.3f ms, event %.3f ms" % (w3p, e3p))
+        if "bwd" in only:
+            # its backward (swa_bwd_varlen), for a seeded output gradient
+            gen = torch.Generator(device="cpu").manual_seed(3 + 7919)
+            dop = (torch.randn(op.shape, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+            lsp = torch.empty(op.shape[:2], dtype=torch.float32, device=dev)
+            swa.swa_fwd_varlen(pk[0], pk[1], pk[2], op, 4096, md3, cu, lse=lsp)
+            gq, gk, gv = (torch.empty_like(t) for t in pk)
+            wsp = torch.empty(swa.swa_bwd_workspace_size(1, H3, op.shape[0]) // 4,
+                              dtype=torch.float32, device=dev)
+            fbp = lambda: swa.swa_bwd_varlen(pk[0], pk[1], pk[2], op, dop, lsp, gq, gk, gv, wsp,
+                                             4096, md3, cu)
+            wbp, ebp, _ = timed(fbp, 3, 1)
+            out["gqa_bwd_packed"] = dict(wall_ms=wbp, kernel_ms=ebp,
+                                         flops=2.5 * out["gqa"]["flops"], tokens=int(sum(lens)))
+            log("gqa packed bwd: wall %.3f ms, event %.3f ms" % (wbp, ebp))
+            del dop, lsp, gq, gk, gv, wsp
         del pk, op
 
     # ---------------- chunked prefill against the ring -------------
@@ -530,6 +546,15 @@ def main():
                                       "TFLOP_per_s": round(t, 2),
                                       "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                       "ms_per_step": round(gp["wall_ms"], 4)}
+    if "gqa_bwd_packed" in out:
+        gb = out["gqa_bwd_packed"]
+        t = gb["flops"] / (gb["wall_ms"] * 1e-3) / 1e12
+        line["backward_gqa_packed"] = {"workload": "backward of the packed GQA workload "
+                                                   "(swa_bwd_varlen, %d tokens), useful FLOPs "
+                                                   "= 2.5 x forward" % gb["tokens"],
+                                       "TFLOP_per_s": round(t, 2),
+                                       "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                       "ms_per_step": round(gb["wall_ms"], 4)}
     if "chunk_sink" in out:
         cs = out["chunk_sink"]
         t = cs["flops"] / (cs["wall_ms"] * 1e-3) / 1e12
