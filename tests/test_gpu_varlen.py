@@ -163,3 +163,56 @@ def test_bwd_varlen_empty_sequences_mha():
         assert got.shape == ref.shape and np.all(np.isfinite(got)), nm
         err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (nm, float(err.max()))
+
+
+def test_bwd_varlen_gqa_workload_sampled():
+    """The packed backward at the size the benchmark times: the GQA workload's
+    four sequences (H=32, Hkv=8, W=4096, 76 563 tokens) packed token-major,
+    sampled dq rows and dk/dv keys against the oracle's selected-entry
+    gradients of the same sequences in padded form."""
+    inp = synth.make("prefill_gqa")
+    lens = [int(x) for x in inp["q_len"]]
+    B, H, N, d = inp["q"].shape
+    Hkv, W = inp["k"].shape[1], 4096
+    pack = lambda x: torch.cat([x[b, :, :n].transpose(0, 1) for b, n in enumerate(lens)]
+                               ).contiguous()
+    q, k, v = (pack(inp[n]).to(DEV) for n in ("q", "k", "v"))
+    total = q.shape[0]
+    gen = torch.Generator(device="cpu").manual_seed(2024)
+    do_cpu = (torch.randn((total, H, d), generator=gen) * 0.5).to(torch.bfloat16)
+    do = do_cpu.to(DEV)
+    cu_np = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(cu_np).to(DEV)
+    meta = swa.swa_blockmask_build(B, N, N, W, 128, 64, q_len=lens, k_len=lens)
+    md = swa.meta_to_device(meta, DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty((total, H), dtype=torch.float32, device=DEV)
+    swa.swa_fwd_varlen(q, k, v, o, W, md, cu, lse=lse)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    ws = torch.empty(swa.swa_bwd_workspace_size(1, H, total) // 4, device=DEV)
+    swa.swa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, W, md, cu)
+    torch.cuda.synchronize()
+    del q, k, v, o, do, lse, ws
+    # the output gradient in the oracle's padded layout (zero past each length)
+    dout = np.zeros((B, H, N, d))
+    for b, n in enumerate(lens):
+        dout[b, :, :n] = f64(do_cpu[cu_np[b]:cu_np[b + 1]]).transpose(1, 0, 2)
+    rng = np.random.default_rng(31)
+    rows, keys = [], []
+    for b, n in enumerate(lens):
+        rows += [[b, int(h), int(i)] for h, i in zip(rng.integers(0, H, 12), rng.integers(0, n, 12))]
+        rows += [[b, 0, 0], [b, H - 1, n - 1], [b, 5, W - 1], [b, 6, W]]
+        # a key is costly for the oracle in proportion to the rows that see it
+        # (up to G*W): random keys near the end, and two that W rows see
+        keys += [[b, int(g), int(j)] for g, j in zip(rng.integers(0, Hkv, 2),
+                                                     rng.integers(n - 300, n, 2))]
+        keys += [[b, 0, 0], [b, Hkv - 1, n - 1], [b, 3, n - W]]
+    rq, rk, rv = oracle.bwd_sel(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), dout, W,
+                                1 / math.sqrt(d), rows, keys, q_len=np.array(lens, dtype=np.int32))
+    gq = np.stack([f64(dq[cu_np[b] + i, h]) for b, h, i in rows])
+    gk = np.stack([f64(dk[cu_np[b] + j, g]) for b, g, j in keys])
+    gv = np.stack([f64(dv[cu_np[b] + j, g]) for b, g, j in keys])
+    assert all(np.all(np.isfinite(t)) for t in (f64(dq), f64(dk), f64(dv))), "unwritten rows"
+    for got, ref, nm in ((gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")):
+        err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, ("GQA packed " + nm, float(err.max()))
