@@ -14,13 +14,19 @@
 // LDS reads, one 32-key half after the other (so that two waves fit per
 // SIMD).  Each lane holds one query column: lse and D are per lane.
 //
-// dkdv_kernel: one workgroup per (key tile of 64, kv head, request), 32 keys
-// per wave held in registers, visiting 64-row steps of every query head of
-// the group in the query tiles whose class-grid entry for the key tile is
-// live (Q, dO, lse and D rows staged in LDS, double-buffered).  Per 32-row
-// block: S = Q K^T and dP = dO V^T (A = Q or dO rows from LDS, B = the wave's
-// K or V rows), P and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T
-// and Q^T read by transposing LDS reads.  Each lane holds one key column.
+// dkdv_kernel: one workgroup of four waves per (key tile of 64, kv head,
+// request), visiting 64-row steps of every query head of the group in the
+// query tiles whose class-grid entry for the key tile is live (Q, dO, lse and
+// D rows staged in LDS, double-buffered).  The waves split the work by role,
+// two per role, one per 32-key half: role 0 holds its keys' K rows and
+// computes S = Q K^T, P (masked) and dV^T += dO^T P; role 1 holds the V rows
+// and computes dP = dO V^T, then dS = P (dP - D) and dK^T += Q^T dS.  P goes
+// from role 0 to role 1 through LDS, once per step, across a barrier that
+// waits for LDS writes only.  A wave then holds one operand row set and one
+// accumulator set (252 registers at D = 128), so two waves run per SIMD, where
+// one wave holding K, V, dK and dV needed 316 and ran alone.  Each lane holds
+// one key column; A operands are Q or dO rows from LDS, and dO^T, Q^T come
+// from transposing LDS reads.
 //
 // PK (packed batch): the same kernels over token-major tensors, sequence b
 // being tokens cu[b] .. cu[b+1]-1; rows are then H*D (Q side) or Hkv*D (K
@@ -330,16 +336,30 @@ void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Barrier for a hand-off through LDS only: waits for this wave's LDS writes,
+// not for its global loads in flight (the next step's staging continues).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D, bool PK>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_kernel(BwdArgs a) {
-    constexpr int NW = 2, KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
+    constexpr int NW = 4, KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
     // stage: [Q rows | dO rows | lse[64] | D[64]]
     __shared__ __attribute__((aligned(1024))) char stage0[2 * TILEB + 512];
     __shared__ __attribute__((aligned(1024))) char stage1[2 * TILEB + 512];
+    // P of the current step, from the waves that compute it to the waves that
+    // need it for dS: [key half][32-row block][lane][16 bf16]
+    __shared__ __attribute__((aligned(16))) u32x4 xch[2][2][64][2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // role 0 waves hold K and compute S, P and dV; role 1 waves hold V and
+    // compute dP, dS and dK; kh: which 32 keys of the tile
+    const int role = wave >> 1, kh = wave & 1;
     const int lq = lane & 31, hh = lane >> 5;
     const int N = a.N, W = a.W;
     const int nkt = (N + BN - 1) / BN;
@@ -353,19 +373,17 @@ void dkdv_kernel(BwdArgs a) {
     const int tq = a.tile_q;
     const int nqt = (N + tq - 1) / tq;
 
-    const int mykey = kt * BN + wave * 32 + lq;
+    const int mykey = kt * BN + kh * 32 + lq;
     // index of this key in the [.][Hkv][N] (or [tokens][Hkv]) row arrays
     const size_t keyidx =
         PK ? (size_t)(cub + mykey) * a.Hkv + g : ((size_t)b * a.Hkv + g) * N + mykey;
-    bf16x8 kf[KS], vf[KS];
+    bf16x8 op[KS];  // this lane's K row (role 0) or V row (role 1)
     {
-        const __bf16 *kp = (const __bf16 *)a.k + keyidx * D;
-        const __bf16 *vp = (const __bf16 *)a.v + keyidx * D;
+        const __bf16 *src = (const __bf16 *)(role == 0 ? a.k : a.v) + keyidx * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             const u32x4 z = {0, 0, 0, 0};
-            kf[ks] = __builtin_bit_cast(bf16x8, (mykey < nrows) ? ld16(kp + ks * 16 + hh * 8) : z);
-            vf[ks] = __builtin_bit_cast(bf16x8, (mykey < nrows) ? ld16(vp + ks * 16 + hh * 8) : z);
+            op[ks] = __builtin_bit_cast(bf16x8, (mykey < nrows) ? ld16(src + ks * 16 + hh * 8) : z);
         }
     }
     // visible query rows of this lane's key: [ka, kb_] (every later row for an
@@ -374,14 +392,11 @@ void dkdv_kernel(BwdArgs a) {
     const bool kempty = mykey >= qlen || kb_ < ka;
     const float c2 = a.scale * LOG2E;
 
-    f32x16 dkacc[DB], dvacc[DB];
+    f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1) of this lane's key
 #pragma unroll
     for (int db = 0; db < DB; db++)
 #pragma unroll
-        for (int e = 0; e < 16; e++) {
-            dkacc[db][e] = 0.f;
-            dvacc[db][e] = 0.f;
-        }
+        for (int e = 0; e < 16; e++) acc[db][e] = 0.f;
 
     // steps: (query head h, 64-row block s0) over query tiles whose class-grid
     // entry for this key tile is live, rows kt*64 .. kt*64+63+W-1 at most
@@ -390,7 +405,6 @@ void dkdv_kernel(BwdArgs a) {
                                            : (int)min((long)nqt - 1, ((long)kt * BN + BN - 2 + W) / tq);
     const int spt = (tq + BN - 1) / BN;  // 64-row steps per query tile
     const uint8_t *clsb = a.cls + (size_t)b * nqt * nkt;
-    // step index t over (h, qt, sub); returns the next live step at or after t
     const int qtn = qt_hi - qt_lo + 1;
     const int nsteps = G * qtn * spt;
     // the class-grid column of this key tile over [qt_lo, qt_hi], read once
@@ -436,8 +450,10 @@ void dkdv_kernel(BwdArgs a) {
         stage_rows<D, NW>((const __bf16 *)a.dout + rb * D, s0, nrows, rst * ROWB, dst + TILEB,
                           wave, lane);
         // row values of the 64 rows (zeros past the data, which is masked)
-        const float *src = (wave == 0) ? (a.lse + rb) : (a.dvec + rb);
-        stage_vals(src, s0 + lane, nrows, rst, dst + 2 * TILEB + wave * 256);
+        if (wave < 2) {
+            const float *src = (wave == 0) ? (a.lse + rb) : (a.dvec + rb);
+            stage_vals(src, s0 + lane, nrows, rst, dst + 2 * TILEB + wave * 256);
+        }
     };
 
     const int tr_j = lane & 15;
@@ -455,61 +471,142 @@ void dkdv_kernel(BwdArgs a) {
         const char *dsm = cur + TILEB;
         const float *lsm = (const float *)(cur + 2 * TILEB);
         const float *Dsm = lsm + 64;
-        // the two 32-row blocks run as a loop: unrolled, the compiler hoisted
-        // both blocks' LDS fragments and addresses and spilled 48 registers
-        // (with them in the loop: 181 VGPRs + the AGPRs, no scratch)
-#pragma unroll 1
-        for (int rb = 0; rb < 2; rb++) {
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 s, dp;
+        // lane constants of the LDS addresses, made opaque per step (lzs is an
+        // opaque 0) so that the compiler recomputes each fragment address near
+        // its read instead of keeping dozens of them live across the loop
+        int lzs;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(lzs));
+        const int lqs = lq + lzs, trr = tr_row + lzs, trc = tr_col + lzs;
+        // carried across the hand-off, 16 dwords of bf16 pairs: role 0 its P of
+        // both 32-row blocks, role 1 its dP - D of both blocks (rounded to bf16
+        // like the dS it becomes: a relative error of the same size)
+        f32x16 hold;
+        if (role == 0) {
+            // S = Q K^T, P = exp(S - lse) (0 where masked), handed to role 1
 #pragma unroll
-            for (int e2 = 0; e2 < 16; e2++) {
-                s[e2] = 0.f;
-                dp[e2] = 0.f;
-            }
+            for (int rb = 0; rb < 2; rb++) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 s;
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qsm, rb * 32, lq, hh, ks),
-                                                            kf[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dsm, rb * 32, lq, hh, ks),
-                                                             vf[ks], dp, 0, 0, 0);
-                if (ks & 1) __builtin_amdgcn_sched_barrier(0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // rows of C element 4i+j: q = s0 + rb*32 + 8i + 4hh + j
-            const int qb = s0 + rb * 32 + 4 * hh;
-            const int L1 = kempty ? -(1 << 20) : ka - qb;
-            const uint32_t n1 = kempty ? 0u : (uint32_t)(kb_ - ka);
-            bf16x8 pk[2], dsk[2];
+                for (int e2 = 0; e2 < 16; e2++) s[e2] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const f32x4 lse4 = *(const f32x4 *)(lsm + rb * 32 + 8 * i + 4 * hh);
-                const f32x4 D4 = *(const f32x4 *)(Dsm + rb * 32 + 8 * i + 4 * hh);
+                for (int ks = 0; ks < KS; ks++)
+                {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qsm, rb * 32, lqs, hh, ks),
+                                                                op[ks], s, 0, 0, 0);
+                    if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+                }
+                // rows of C element 4i+j: q = s0 + rb*32 + 8i + 4hh + j
+                const int qb = s0 + rb * 32 + 4 * hh;
+                const int L1 = kempty ? -(1 << 20) : ka - qb;
+                const uint32_t n1 = kempty ? 0u : (uint32_t)(kb_ - ka);
+                bf16x8 pk[2];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int c = 8 * i + j;
-                    const bool vis = !part || ((uint32_t)(c - L1) <= n1);
-                    const float p =
-                        vis ? __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], c2, -lse4[j] * LOG2E)) : 0.f;
-                    const float ds = p * (dp[4 * i + j] - D4[j]);
-                    // k index hh*8 + 4r + t of 16-row step kk = q 16kk + 8r + 4hh + t
-                    pk[i >> 1][4 * (i & 1) + j] = (__bf16)p;
-                    dsk[i >> 1][4 * (i & 1) + j] = (__bf16)ds;
+                for (int i = 0; i < 4; i++) {
+                    const f32x4 lse4 = *(const f32x4 *)(lsm + rb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int c = 8 * i + j;
+                        const bool vis = !part || ((uint32_t)(c - L1) <= n1);
+                        const float p =
+                            vis ? __builtin_amdgcn_exp2f(fmaf(s[4 * i + j], c2, -lse4[j] * LOG2E))
+                                : 0.f;
+                        // k index hh*8 + 4r + t of 16-row step kk = q 16kk + 8r + 4hh + t
+                        pk[i >> 1][4 * (i & 1) + j] = (__bf16)p;
+                    }
+                }
+                const u32x4 w0 = __builtin_bit_cast(u32x4, pk[0]);
+                const u32x4 w1 = __builtin_bit_cast(u32x4, pk[1]);
+                xch[kh][rb][lane][0] = w0;
+                xch[kh][rb][lane][1] = w1;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    hold[rb * 8 + e2] = __uint_as_float(w0[e2]);
+                    hold[rb * 8 + 4 + e2] = __uint_as_float(w1[e2]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            // dP = dO V^T
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++)
+            for (int rb = 0; rb < 2; rb++) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 dp;
 #pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_frag<D>(dsm + rb * 32 * ROWB, kk, db, tr_row, tr_col), pk[kk],
-                        dvacc[db], 0, 0, 0);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_frag<D>(qsm + rb * 32 * ROWB, kk, db, tr_row, tr_col), dsk[kk],
-                        dkacc[db], 0, 0, 0);
-                    if (db & 1) __builtin_amdgcn_sched_barrier(0);
+                for (int e2 = 0; e2 < 16; e2++) dp[e2] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++)
+                {
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        row_frag<D>(dsm, rb * 32, lqs, hh, ks), op[ks], dp, 0, 0, 0);
+                    if (ks & 1) __builtin_amdgcn_sched_barrier(0);
                 }
+                bf16x8 dd[2];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const f32x4 D4 = *(const f32x4 *)(Dsm + rb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) dd[i >> 1][4 * (i & 1) + j] = (__bf16)(dp[4 * i + j] - D4[j]);
+                }
+                const u32x4 w0 = __builtin_bit_cast(u32x4, dd[0]);
+                const u32x4 w1 = __builtin_bit_cast(u32x4, dd[1]);
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    hold[rb * 8 + e2] = __uint_as_float(w0[e2]);
+                    hold[rb * 8 + 4 + e2] = __uint_as_float(w1[e2]);
+                }
+            }
+        }
+        lds_barrier();
+        if (role == 0) {
+            // dV^T += dO^T P
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                u32x4 w0, w1;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    w0[e2] = __float_as_uint(hold[rb * 8 + e2]);
+                    w1[e2] = __float_as_uint(hold[rb * 8 + 4 + e2]);
+                }
+                const bf16x8 pk[2] = {__builtin_bit_cast(bf16x8, w0), __builtin_bit_cast(bf16x8, w1)};
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                    for (int db = 0; db < DB; db++) {
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_frag<D>(dsm + rb * 32 * ROWB, kk, db, trr, trc), pk[kk],
+                            acc[db], 0, 0, 0);
+                        if (db & 1) __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+        } else {
+            // dS = P (dP - D), dK^T += Q^T dS
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                const bf16x8 pk[2] = {__builtin_bit_cast(bf16x8, xch[kh][rb][lane][0]),
+                                      __builtin_bit_cast(bf16x8, xch[kh][rb][lane][1])};
+                u32x4 w0, w1;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    w0[e2] = __float_as_uint(hold[rb * 8 + e2]);
+                    w1[e2] = __float_as_uint(hold[rb * 8 + 4 + e2]);
+                }
+                const bf16x8 dd[2] = {__builtin_bit_cast(bf16x8, w0), __builtin_bit_cast(bf16x8, w1)};
+                bf16x8 dsk[2];
+#pragma unroll
+                for (int x = 0; x < 2; x++)
+#pragma unroll
+                    for (int t = 0; t < 8; t++)
+                        dsk[x][t] = (__bf16)((float)pk[x][t] * (float)dd[x][t]);
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                    for (int db = 0; db < DB; db++) {
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_frag<D>(qsm + rb * 32 * ROWB, kk, db, trr, trc), dsk[kk],
+                            acc[db], 0, 0, 0);
+                        if (db & 1) __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
         }
     };
     int t = live_from(0);
@@ -524,20 +621,17 @@ void dkdv_kernel(BwdArgs a) {
     }
 
     if (mykey < nrows) {
-        __bf16 *kp = (__bf16 *)a.dk + keyidx * D;
-        __bf16 *vp = (__bf16 *)a.dv + keyidx * D;
+        // role 0 writes dV, role 1 dK (scaled)
+        __bf16 *dst = (__bf16 *)(role == 0 ? a.dv : a.dk) + keyidx * D;
+        const float f = role == 0 ? 1.f : a.scale;
 #pragma unroll
         for (int db = 0; db < DB; db++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                bf16x4 wk, wv;
+                bf16x4 w;
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    wk[j] = (__bf16)(dkacc[db][i * 4 + j] * a.scale);
-                    wv[j] = (__bf16)dvacc[db][i * 4 + j];
-                }
-                *(bf16x4 *)(kp + db * 32 + 8 * i + 4 * hh) = wk;
-                *(bf16x4 *)(vp + db * 32 + 8 * i + 4 * hh) = wv;
+                for (int j = 0; j < 4; j++) w[j] = (__bf16)(acc[db][i * 4 + j] * f);
+                *(bf16x4 *)(dst + db * 32 + 8 * i + 4 * hh) = w;
             }
     }
 }
@@ -555,7 +649,7 @@ hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
     else
         hipLaunchKernelGGL((dq_kernel<D, 2, PK>), dim3((unsigned)gq), dim3(128), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((dkdv_kernel<D, PK>), dim3((unsigned)gk), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, PK>), dim3((unsigned)gk), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
