@@ -61,17 +61,20 @@ __device__ __forceinline__ int xcd_remap(int p, int T) {
     return x * q + (x < r ? x : r) + i;
 }
 
-// Workgroups go to the XCDs round-robin, about 64 per XCD at a time: in round
-// r XCD x runs the 64-item chunk 8r + (x + r) % 8 of the logical order, so the
-// items an XCD runs together are neighbours (shared tiles in its L2) and every
-// XCD draws from all parts of the order (even work when sequence lengths
-// differ).  The tail of T mod 512 items keeps contiguous ranges.  A bijection.
+// Workgroups go to the XCDs round-robin, about 64 per XCD at a time.  The
+// logical order is cut into 64-item chunks and runs of 4 chunks; in rounds
+// 4R .. 4R+3 XCD x runs the chunks of run 8R + (x + R) % 8 in order, so the
+// items an XCD runs together, and its successive chunks, are neighbours
+// (shared tiles in its L2), and every XCD draws from all parts of the order
+// (even work when sequence lengths differ).  The tail of T mod 2048 items
+// keeps contiguous ranges.  A bijection.
 __device__ __forceinline__ int xcd_deal(int p, int T) {
-    constexpr int C = 64;
-    const int Tm = T / (8 * C) * (8 * C);
+    constexpr int C = 64, S = 4;
+    const int Tm = T / (8 * C * S) * (8 * C * S);
     if (p < Tm) {
         const int x = p & 7, i = p >> 3, r = i / C, o = i % C;
-        return (r * 8 + ((x + r) & 7)) * C + o;
+        const int R = r / S, sub = r % S;
+        return ((R * 8 + ((x + R) & 7)) * S + sub) * C + o;
     }
     return Tm + xcd_remap(p - Tm, T - Tm);
 }

@@ -91,20 +91,26 @@ __device__ __forceinline__ int xcd_remap(int p, int T) {
 }
 
 // Workgroups go to the 8 XCDs round-robin (p % 8), each XCD running about 64
-// at a time.  The logical order is cut into chunks of 64 tiles; in round r
-// (its workgroups 64r .. 64r+63) XCD x runs chunk 8r + (x + r) % 8.  The 64
+// at a time.  The logical order is cut into chunks of 64 tiles and runs of
+// S = 4 consecutive chunks; in rounds 4R .. 4R+3 (its workgroups 256R ..
+// 256R+255) XCD x runs the chunks of run 8R + (x + R) % 8, in order.  The 64
 // workgroups an XCD runs together stay neighbours in the logical order (they
-// share K/V tiles in its L2), while every XCD draws its chunks from all parts
-// of the order, so work that varies along it (sequences of different
-// lengths) is shared out evenly; contiguous ranges per XCD left one XCD with
-// 1.7x the mean work on the GQA workload.  A tail of T mod 512 tiles keeps
-// contiguous ranges.  A bijection on [0, T).
+// share K/V tiles in its L2), and so do its successive chunks: with long
+// windows the K/V span of a chunk overlaps the next chunk's by most of the
+// window, which the XCD's L2 then still holds (one chunk per XCD per round
+// fetched each K/V tile from HBM about 2.75 times on the GQA workload).
+// Every XCD still draws its runs from all parts of the order, so work that
+// varies along it (sequences of different lengths) is shared out evenly;
+// contiguous ranges per XCD left one XCD with 1.7x the mean work on the GQA
+// workload.  A tail of T mod 2048 tiles keeps contiguous ranges.  A
+// bijection on [0, T).
 __device__ __forceinline__ int xcd_deal(int p, int T) {
-    constexpr int C = 64;
-    const int Tm = T / (8 * C) * (8 * C);
+    constexpr int C = 64, S = 4;
+    const int Tm = T / (8 * C * S) * (8 * C * S);
     if (p < Tm) {
         const int x = p & 7, i = p >> 3, r = i / C, o = i % C;
-        return (r * 8 + ((x + r) & 7)) * C + o;
+        const int R = r / S, sub = r % S;
+        return ((R * 8 + ((x + R) & 7)) * S + sub) * C + o;
     }
     return Tm + xcd_remap(p - Tm, T - Tm);
 }
