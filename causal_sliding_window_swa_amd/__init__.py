@@ -336,7 +336,7 @@ def swa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, q_len=None, s
 
 def swa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, W, meta, cu_seqlens,
                    scale=None, stream=None):
-    """Gradients of swa_fwd_varlen (bf16).  q,o,dout,dq [total,H,d]; k,v,dk,dv
+    """Gradients of swa_fwd_varlen.  q,o,dout,dq [total,H,d]; k,v,dk,dv
     [total,Hkv,d] token-major; lse fp32 [total,H] from swa_fwd_varlen; meta and
     cu_seqlens as for swa_fwd_varlen; workspace: device tensor of at least
     swa_bwd_workspace_size(1, H, total) bytes."""

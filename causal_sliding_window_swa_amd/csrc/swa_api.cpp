@@ -231,8 +231,6 @@ extern "C" int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
                     total, max_len);
     if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if (dt != SWA_BF16)
-        return fail(SWA_EUNSUPPORTED, "%s: the packed backward is bf16 only", fn);
     if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
     // query-side rows are H * d elements apart (the wider of the two strides)
     if ((rc = check_span(fn, dt, max_len, 2LL * d * H))) return rc;
@@ -258,7 +256,7 @@ extern "C" int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
     a.dvec = (float *)workspace;
     a.n_sink = n_sink;
     a.scale = scale;
-    a.bf16 = 1;
+    a.bf16 = dt == SWA_BF16;
     return launched(fn, swa::launch_bwd(a, (hipStream_t)stream));
 }
 

@@ -16,7 +16,10 @@
 // row; a key visits the query tiles whose class-grid entry for its key tile
 // is live.  This is the fp32-arithmetic path for both dtypes: one wave per
 // query row (dQ) or per key (dK, dV), the head dim spread over the lanes and
-// dot products reduced across the wave.
+// dot products reduced across the wave.  A packed batch (cu set) runs over
+// the same padded index space of longest-sequence length, with rows and keys
+// past a sequence's end skipped and every access mapped to the token-major
+// layout (qrow, krow).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -42,13 +45,32 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Rows of request b that exist: N when padded, its own length when packed.
+__device__ __forceinline__ int rows_of(const BwdArgs &a, int b) {
+    return a.cu ? a.cu[b + 1] - a.cu[b] : a.N;
+}
+// Index of row i of head h of request b in the query-side row arrays (q, o,
+// dout, dq in units of d; lse, dvec): [B][H][N] padded, [tokens][H] packed.
+__device__ __forceinline__ size_t qrow(const BwdArgs &a, int b, int h, int i) {
+    return a.cu ? (size_t)(a.cu[b] + i) * a.H + h : ((size_t)b * a.H + h) * a.N + i;
+}
+// Index of key j of kv head g of request b in k, v, dk, dv (units of d).
+__device__ __forceinline__ size_t krow(const BwdArgs &a, int b, int g, int j) {
+    return a.cu ? (size_t)(a.cu[b] + j) * a.Hkv + g : ((size_t)b * a.Hkv + g) * a.N + j;
+}
+
 // D_i = <dO_i, O_i>: one wave per row, lanes over the head dim.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dvec_kernel(BwdArgs a) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long lrow = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long rows = (long)a.B * a.H * a.N;
-    if (row >= rows) return;
+    if (lrow >= rows) return;
+    const int i = (int)(lrow % a.N);
+    const int h = (int)((lrow / a.N) % a.H);
+    const int b = (int)(lrow / ((long)a.N * a.H));
+    if (i >= rows_of(a, b)) return;
+    const size_t row = qrow(a, b, h, i);
     const T *o = (const T *)a.o + row * a.d;
     const T *dO = (const T *)a.dout + row * a.d;
     float acc = 0.f;
@@ -60,16 +82,18 @@ __global__ __launch_bounds__(256) void bwd_dvec_kernel(BwdArgs a) {
 // dQ: one wave per query row (b, h, i); keys from the CSR row of its tile.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long lrow = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long rows = (long)a.B * a.H * a.N;
-    if (row >= rows) return;
+    if (lrow >= rows) return;
     const int N = a.N, d = a.d, W = a.W;
-    const int i = (int)(row % N);
-    const int h = (int)((row / N) % a.H);
-    const int b = (int)(row / ((long)N * a.H));
+    const int i = (int)(lrow % N);
+    const int h = (int)((lrow / N) % a.H);
+    const int b = (int)(lrow / ((long)N * a.H));
     const int g = h / (a.H / a.Hkv);
-    const int qlen = a.q_len ? a.q_len[b] : N;
+    if (i >= rows_of(a, b)) return;  // past a packed sequence: another sequence's row
+    const int qlen = a.cu ? rows_of(a, b) : (a.q_len ? a.q_len[b] : N);
+    const size_t row = qrow(a, b, h, i);
     T *dq = (T *)a.dq + row * d;
     float qv[2] = {0.f, 0.f}, dov[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
     if (i < qlen && a.lse[row] != -INFINITY) {
@@ -82,9 +106,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
                 dov[u] = ld(dO, lane + 64 * u);
             }
         const float c2 = a.scale * LOG2E, lse2 = a.lse[row] * LOG2E, Dr = a.dvec[row];
-        const size_t kvh = ((size_t)b * a.Hkv + g) * N;
-        const T *kb = (const T *)a.k + kvh * d;
-        const T *vb = (const T *)a.v + kvh * d;
+        // key j of this row's kv head at kb + j * ks (ks = d, or Hkv*d packed)
+        const size_t ks = a.cu ? (size_t)a.Hkv * d : (size_t)d;
+        const T *kb = (const T *)a.k + krow(a, b, g, 0) * d;
+        const T *vb = (const T *)a.v + krow(a, b, g, 0) * d;
         const int nqt = (N + a.tile_q - 1) / a.tile_q;
         const int qt = i / a.tile_q;
         const int e0 = a.row_ptr[b * nqt + qt], e1 = a.row_ptr[b * nqt + qt + 1];
@@ -99,9 +124,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int u = 0; u < 2; u++)
                     if (lane + 64 * u < d) {
-                        kv[u] = ld(kb, (size_t)j * d + lane + 64 * u);
+                        kv[u] = ld(kb, (size_t)j * ks + lane + 64 * u);
                         s += qv[u] * kv[u];
-                        dp += dov[u] * ld(vb, (size_t)j * d + lane + 64 * u);
+                        dp += dov[u] * ld(vb, (size_t)j * ks + lane + 64 * u);
                     }
                 s = wave_sum(s);
                 dp = wave_sum(dp);
@@ -121,16 +146,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // in the query tiles whose class-grid entry for the key's tile is live.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
-    const long key = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long lkey = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long keys = (long)a.B * a.Hkv * a.N;
-    if (key >= keys) return;
+    if (lkey >= keys) return;
     const int N = a.N, d = a.d, W = a.W;
-    const int j = (int)(key % N);
-    const int g = (int)((key / N) % a.Hkv);
-    const int b = (int)(key / ((long)N * a.Hkv));
+    const int j = (int)(lkey % N);
+    const int g = (int)((lkey / N) % a.Hkv);
+    const int b = (int)(lkey / ((long)N * a.Hkv));
     const int G = a.H / a.Hkv;
-    const int qlen = a.q_len ? a.q_len[b] : N;
+    if (j >= rows_of(a, b)) return;  // past a packed sequence: another sequence's key
+    const int qlen = a.cu ? rows_of(a, b) : (a.q_len ? a.q_len[b] : N);
+    const size_t key = krow(a, b, g, j);
     T *dk = (T *)a.dk + key * d;
     T *dv = (T *)a.dv + key * d;
     float kv[2] = {0.f, 0.f}, vv[2] = {0.f, 0.f}, ak[2] = {0.f, 0.f}, av[2] = {0.f, 0.f};
@@ -159,9 +186,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             const int i1 = min(min((qt + 1) * a.tile_q - 1, (j < a.n_sink) ? qlen - 1 : j + W - 1),
                                qlen - 1);
             for (int h = g * G; h < (g + 1) * G; h++) {
-                const size_t rbase = ((size_t)b * a.H + h) * N;
                 for (int i = i0; i <= i1; i++) {
-                    const size_t row = rbase + i;
+                    const size_t row = qrow(a, b, h, i);
                     const T *q = (const T *)a.q + row * d;
                     const T *dO = (const T *)a.dout + row * d;
                     float s = 0.f, dp = 0.f, qv[2] = {0.f, 0.f}, dov[2] = {0.f, 0.f};
@@ -211,8 +237,6 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
-    // a packed batch runs on the bf16 MFMA kernels only
-    if (a.cu) return bwd_bf16_supported(a) ? launch_bwd_bf16(a, s) : hipErrorNotSupported;
     if (!a.bf16) return launch_t<float>(a, s);
     if (!bwd_bf16_supported(a)) return launch_t<__bf16>(a, s);
     // the MFMA dq kernel computes the row values D itself

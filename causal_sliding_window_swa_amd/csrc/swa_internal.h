@@ -87,8 +87,7 @@ struct BwdArgs {
     const int32_t *cu;
 };
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
-// bf16 MFMA kernels (swa_bwd_bf16.hip): d in {64, 128}, tile_k 64, tile_q in {64, 128};
-// the only kernels that take a packed batch.
+// bf16 MFMA kernels (swa_bwd_bf16.hip): d in {64, 128}, tile_k 64, tile_q in {64, 128}.
 bool bwd_bf16_supported(const BwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 

@@ -207,8 +207,10 @@ int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
  * Every output row is written; no padding is read or written.  The kernels
  * do not re-check cu_seqlens against the metadata: inconsistent ones are a
  * caller error.
- * Supported: dt = SWA_BF16, d in {64, 128}, (tile_q, tile_k) = (128, 64) or
- * (64, 64), max_len * H * d * 2 < 2^31; anything else is SWA_EUNSUPPORTED.
+ * Supported: as swa_fwd_varlen for dt, d and tiles (bf16: d in {64, 128},
+ * (tile_q, tile_k) = (128, 64) or (64, 64), on the MFMA kernels, with
+ * max_len * H * d * 2 < 2^31; fp32: d % 4 == 0, d <= 128, any positive tiles,
+ * on the fp32-arithmetic kernels); anything else is SWA_EUNSUPPORTED.
  * Errors: SWA_EINVAL (as swa_fwd_varlen, NULL cls_dev, small workspace),
  * SWA_EUNSUPPORTED, SWA_EHIP. */
 int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len, int d, int W,

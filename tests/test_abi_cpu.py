@@ -136,9 +136,9 @@ def test_bwd_varlen_validation_codes():
     assert _bwd_varlen(n_sink=-1) == swa.SWA_EINVAL
     assert _bwd_varlen(cu=False) == swa.SWA_EINVAL
     assert _bwd_varlen(cls=False) == swa.SWA_EINVAL
-    # the packed backward runs on the bf16 MFMA kernels only
-    assert _bwd_varlen(dt=1) == swa.SWA_EUNSUPPORTED
-    assert "bf16" in swa.swa_last_error()
+    # fp32 takes any d % 4 == 0 up to 128 (and any tiles), bf16 d in {64, 128}
+    assert _bwd_varlen(dt=1, d=130) == swa.SWA_EUNSUPPORTED
+    assert _bwd_varlen(dt=1, d=6) == swa.SWA_EUNSUPPORTED
     assert _bwd_varlen(d=96) == swa.SWA_EUNSUPPORTED
     assert _bwd_varlen(tq=32) == swa.SWA_EUNSUPPORTED
     assert _bwd_varlen(tk=128) == swa.SWA_EUNSUPPORTED

@@ -216,3 +216,37 @@ def test_bwd_varlen_gqa_workload_sampled():
     for got, ref, nm in ((gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")):
         err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, ("GQA packed " + nm, float(err.max()))
+
+
+def test_bwd_varlen_fp32():
+    """The fp32 packed backward (fp32-arithmetic kernels) with odd tiles and
+    head dim, grouped heads, sinks and a zero-length sequence, against the
+    oracle's padded backward in packed order at the fp32 bar."""
+    lens = [70, 0, 3, 41]
+    B, N, H, Hkv, d = len(lens), max(lens), 4, 2, 20
+    inp = synth.gen_bwd(B, H, Hkv, N, d, seed=77, std=1.0, dtype="f32")
+    pack = lambda x: torch.cat([x[b, :, :L].transpose(0, 1) for b, L in enumerate(lens)]
+                               ).contiguous()
+    q, k, v, do = (pack(inp[n]).to(DEV) for n in ("q", "k", "v", "dout"))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    total = q.shape[0]
+    L = np.array(lens, dtype=np.int32)
+    for W, S, tq, tk in ((5, 0, 8, 8), (13, 3, 7, 5), (80, 2, 16, 16)):
+        meta = swa.swa_blockmask_build(B, N, N, W, tq, tk, q_len=lens, k_len=lens, n_sink=S)
+        md = swa.meta_to_device(meta, DEV)
+        o = torch.empty_like(q)
+        lse = torch.empty((total, H), dtype=torch.float32, device=DEV)
+        swa.swa_fwd_varlen(q, k, v, o, W, md, cu, lse=lse)
+        dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+        ws = torch.empty(swa.swa_bwd_workspace_size(1, H, total) // 4, device=DEV)
+        swa.swa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, W, md, cu)
+        torch.cuda.synchronize()
+        rq, rk, rv, _ = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]),
+                                   f64(inp["dout"]), W, 1 / math.sqrt(d), q_len=L, n_sink=S)
+        packed = lambda r: np.concatenate([r[b, :, :n].transpose(1, 0, 2)
+                                           for b, n in enumerate(lens)])
+        for got, ref, nm in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+            ref, got = packed(ref), f64(got)
+            assert np.all(np.isfinite(got)), ("unwritten rows", W, S, nm)
+            err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
+            assert err.max() <= 1e-4, ("fp32 packed bwd", W, S, nm, float(err.max()))
