@@ -17,22 +17,29 @@
 namespace swa {
 namespace {
 
-// Copy new rows t in [t0, Tq) of k_new/v_new into their ring slots.
-// grid (Tq - t0, Hkv, B); one row of d elements per block.
-__global__ void ring_write_kernel(CommitArgs a, int t0) {
-    const int t = t0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy new rows t in [t0, Tq) of k_new/v_new into their ring slots.  One
+// thread per 16-byte piece of a row (rows are d * elem_bytes long, a multiple
+// of 16 for every supported d and dtype, and the buffers are 16-byte
+// aligned); consecutive threads take consecutive pieces of rows (b, g, t) in
+// k_new order, so reads and writes coalesce.
+__global__ __launch_bounds__(256) void ring_write_kernel(CommitArgs a, int t0) {
+    const int P = (int)((size_t)a.d * a.elem_bytes / 16);  // pieces per row
+    const int nt = a.Tq - t0;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)nt * a.Hkv * a.B * P) return;
+    const int pc = (int)(idx % P);
+    const long r = idx / P;
+    const int t = t0 + (int)(r % nt);
+    const int g = (int)((r / nt) % a.Hkv);
+    const int b = (int)(r / ((long)nt * a.Hkv));
     const int W = a.W;
     const int slot = (int)(((int64_t)a.ring_start[b] + a.cache_len[b] + t) % W);
-    const size_t row_bytes = (size_t)a.d * a.elem_bytes;
     const size_t kvh = (size_t)b * a.Hkv + g;
-    const char *ks = (const char *)a.k_new + (kvh * a.Tq + t) * row_bytes;
-    const char *vs = (const char *)a.v_new + (kvh * a.Tq + t) * row_bytes;
-    char *kd = (char *)a.kc + (kvh * W + slot) * row_bytes;
-    char *vd = (char *)a.vc + (kvh * W + slot) * row_bytes;
-    for (size_t off = threadIdx.x * 4; off < row_bytes; off += blockDim.x * 4) {
-        *(uint32_t *)(kd + off) = *(const uint32_t *)(ks + off);
-        *(uint32_t *)(vd + off) = *(const uint32_t *)(vs + off);
-    }
+    const size_t src = (kvh * a.Tq + t) * P + pc, dst = (kvh * W + slot) * P + pc;
+    ((u32x4 *)a.kc)[dst] = ((const u32x4 *)a.k_new)[src];
+    ((u32x4 *)a.vc)[dst] = ((const u32x4 *)a.v_new)[src];
 }
 
 // State after appending Tq rows: next_pos += Tq, cache_len = min(W, len+Tq),
@@ -78,8 +85,12 @@ hipError_t launch_sink_write(const CommitArgs &a, hipStream_t s) {
 
 hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s) {
     const int t0 = a.Tq > a.W ? a.Tq - a.W : 0;
-    dim3 grid(a.Tq - t0, a.Hkv, a.B);
-    hipLaunchKernelGGL(ring_write_kernel, grid, dim3(64), 0, s, a, t0);
+    if ((size_t)a.d * a.elem_bytes % 16 != 0) return hipErrorInvalidValue;
+    const long pieces = (long)(a.Tq - t0) * a.Hkv * a.B * (long)((size_t)a.d * a.elem_bytes / 16);
+    const long blocks = (pieces + 255) / 256;
+    if (blocks < 1) return hipSuccess;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(ring_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, t0);
     return hipGetLastError();
 }
 
