@@ -250,3 +250,41 @@ def test_bwd_varlen_fp32():
             assert np.all(np.isfinite(got)), ("unwritten rows", W, S, nm)
             err = np.abs(got - ref) / max(1.0, float(np.abs(ref).max()))
             assert err.max() <= 1e-4, ("fp32 packed bwd", W, S, nm, float(err.max()))
+
+
+@pytest.mark.parametrize("dtype,d,W,S,tq,tk", [("bf16", 128, 100, 4, 128, 64),
+                                               ("bf16", 64, 33, 0, 64, 64),
+                                               ("f32", 20, 13, 3, 7, 5)])
+def test_bwd_varlen_equals_padded(dtype, d, W, S, tq, tk):
+    """The packed backward changes only addressing: on the same sequences its
+    gradients equal the padded backward's (with q_len) bit for bit, rows past
+    each sequence excepted."""
+    lens = [150, 1, 0, 97, 64]
+    B, N, H, Hkv = len(lens), max(lens), 4, 2
+    inp = synth.gen_bwd(B, H, Hkv, N, d, seed=31 + d, dtype=dtype)
+    L = torch.tensor(lens, dtype=torch.int32)
+    meta = swa.swa_blockmask_build(B, N, N, W, tq, tk, q_len=lens, k_len=lens, n_sink=S)
+    md = swa.meta_to_device(meta, DEV)
+    # padded
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "dout"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    swa.swa_fwd(q, k, v, o, W, md, q_len=L.to(DEV), lse=lse)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(swa.swa_bwd_workspace_size(B, H, N) // 4, device=DEV)
+    swa.swa_bwd(q, k, v, o, do, lse, gq, gk, gv, ws, W, md, q_len=L.to(DEV))
+    # packed
+    pack = lambda x: torch.cat([x[b, :, :n].transpose(0, 1) for b, n in enumerate(lens)]
+                               ).contiguous()
+    qp, kp, vp, dop = (pack(x) for x in (q, k, v, do))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    op = torch.empty_like(qp)
+    lsp = torch.empty((qp.shape[0], H), dtype=torch.float32, device=DEV)
+    swa.swa_fwd_varlen(qp, kp, vp, op, W, md, cu, lse=lsp)
+    pq, pk_, pv = (torch.full_like(x, float("nan")) for x in (qp, kp, vp))
+    wsp = torch.empty(swa.swa_bwd_workspace_size(1, H, qp.shape[0]) // 4, device=DEV)
+    swa.swa_bwd_varlen(qp, kp, vp, op, dop, lsp, pq, pk_, pv, wsp, W, md, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(op, pack(o)), "packed forward differs from padded"
+    for got, ref, nm in ((pq, gq, "dq"), (pk_, gk, "dk"), (pv, gv, "dv")):
+        assert torch.equal(got, pack(ref)), nm
