@@ -107,8 +107,8 @@ int swa_blockmask_size(int B, int nq, int nk, int tile_q, int tile_k,
  * Outputs (caller-owned host memory, sizes from swa_blockmask_size):
  * cls [B][nqt][nkt] uint8, row_ptr [B*nqt+1] int32, col [nnz] int32 (key
  * tile index), col_cls [nnz] uint8 (1 full, 2 partial); stats may be NULL.
- * Errors: SWA_EINVAL for W < 1 [Blog §5.1 names "window_size must be
- * positive"], bad sizes, W_ring % tile_k != 0, ring state out of range
+ * Errors: SWA_EINVAL for W < 1 [Blog §5.1: the window has to be at least
+ * one token], bad sizes, W_ring % tile_k != 0, ring state out of range
  * (ring_start not in [0, W_ring), cache_len not in [0, W_ring],
  * next_pos < cache_len), a negative length, or positions that overflow int32. */
 int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q, int tile_k,

@@ -607,6 +607,28 @@ def pin_bwd_selection_matches(O):
         assert np.array_equal(sk[r], dk[b, g, j]) and np.array_equal(sv[r], dv[b, g, j])
 
 
+
+def pin_fwd_rows_matches(O):
+    """The selected-row forward equals the corresponding rows of the full
+    forward, bit for bit: every (b, h, i) of a batch with grouped heads
+    (H = 6 over Hkv = 2), padded lengths (rows past a length included) and
+    attention sinks, requested in a shuffled order so that a row written to
+    the wrong slot, a wrong batch length or a wrong KV group shows."""
+    rng = _rng(47)
+    B, H, Hkv, N, d = 3, 6, 2, 21, 5
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    ql = [21, 9, 1]
+    rows = np.array([[b, h, i] for b in range(B) for h in range(H) for i in range(N)],
+                    dtype=np.int32)
+    rows = rows[rng.permutation(len(rows))]
+    for W, S in ((4, 0), (7, 3), (30, 0), (1, 2)):
+        full = O.fwd(q, k, v, W=W, scale=0.6, q_len=ql, n_sink=S)
+        got = O.fwd_rows(q, k, v, W=W, scale=0.6, rows=rows, q_len=ql, n_sink=S)
+        for r, (b, h, i) in enumerate(rows):
+            assert np.array_equal(got[r], full[b, h, i]), (W, S, b, h, i)
+
 # ---------------------------------------------------------------------------
 # Attention sinks ("Sparse attention taxonomy" §3.2: StreamingLLM keeps the
 # first 4 tokens besides the most recent W, a rule on positions only).
@@ -900,6 +922,7 @@ PINS = [
     pin_bwd_window_mask_autograd,
     pin_bwd_closed_forms,
     pin_bwd_selection_matches,
+    pin_fwd_rows_matches,
     pin_sink_visible_sets,
     pin_sink_pair_counts_and_blocks,
     pin_sink_ring_metadata,

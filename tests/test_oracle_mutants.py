@@ -72,6 +72,11 @@ MUTANTS = {
     "layer_plan_fractional_count": ("if (local) ns++; else nf++;",
                                     "if (local) ns++; else nf++;\n        if (l == L - 1) "
                                     "ns = L * a / (a + b), nf = L - ns;"),
+    # the selected-row forward: the KV group and the valid length of its row
+    "rows_group_interleaved": ("const int64_t g = h / G;\n        const int len = q_len ? q_len[b] : N;",
+                               "const int64_t g = h % Hkv;\n        const int len = q_len ? q_len[b] : N;"),
+    "rows_length_of_first_sequence": ("const int64_t g = h / G;\n        const int len = q_len ? q_len[b] : N;",
+                                      "const int64_t g = h / G;\n        const int len = q_len ? q_len[0] : N;"),
     "csr_row_ptr_shift": ("row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)nnz;",
                           "row_ptr[(int64_t)b * nqt + qt + 1] = (int32_t)(nnz - (nnz > 0));"),
 }
