@@ -119,44 +119,51 @@ def test_fwd_window_locality_bitwise():
     assert torch.equal(o1[:, :, i], o2[:, :, i])
 
 
-def _sample_rows(B, H, N, n, rng, lens=None, extra=()):
-    rows = set(extra)
-    for _ in range(n):
-        b = int(rng.integers(0, B))
-        hi = N if lens is None else int(lens[b]) + 130
-        rows.add((b, int(rng.integers(0, H)), int(rng.integers(0, min(N, hi)))))
-    return np.array(sorted(rows), dtype=np.int32)
-
-
-def test_prefill_workload_sampled():
-    """B=1, H=32, N=8192, W=512, bf16, tiles (128, 64): 2048 sampled rows."""
+def test_prefill_workload_full():
+    """B=1, H=32, N=8192, W=512, bf16, tiles (128, 64): every output element
+    against the oracle's forward of the whole workload (mean-abs over all of it)."""
     inp = synth.make("prefill")
     o, meta = run_fwd(inp, 512, 128, 64)
     assert meta["valid_pairs"] == 32 * 0 + 4063488  # per head; B=1
-    rng = np.random.default_rng(0)
-    rows = _sample_rows(1, 32, 8192, 2048, rng,
-                        extra=[(0, 0, 0), (0, 31, 8191), (0, 5, 511), (0, 5, 512), (0, 7, 4095)])
-    ref = oracle.fwd_rows(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 512, 1 / math.sqrt(128),
-                          rows)
-    got = f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    check(got, ref, torch.bfloat16, "prefill sampled")
+    ref = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 512, 1 / math.sqrt(128))
+    check(o, ref, torch.bfloat16, "prefill workload")
 
 
-def test_prefill_gqa_workload_sampled():
-    """B=4, H=32, Hkv=8, N=32768 padded, W=4096, lengths U[8192, 32768]."""
+def test_prefill_gqa_workload_full():
+    """B=4, H=32, Hkv=8, N=32768 padded, W=4096, lengths U[8192, 32768]: every
+    valid row of every sequence against the oracle (each sequence's forward
+    over its valid length: keys past it are never visible, so the rows are
+    the padded batch's), padded rows exactly 0; and the same sequences packed
+    token-major (swa_fwd_varlen) give the padded call's rows bit for bit."""
     inp = synth.make("prefill_gqa")
     o, meta = run_fwd(inp, 4096, 128, 64)
     L = inp["q_len"].numpy()
-    rng = np.random.default_rng(1)
-    extra = [(b, 0, int(L[b]) - 1) for b in range(4)] + [(b, 31, int(L[b])) for b in range(4)]
-    rows = _sample_rows(4, 32, 32768, 768, rng, lens=L, extra=extra)
-    rows = rows[rows[:, 2] < 32768]
-    ref = oracle.fwd_rows(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 4096,
-                          1 / math.sqrt(128), rows, q_len=L)
-    got = f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    check(got, ref, torch.bfloat16, "gqa sampled")
+    sc = 1 / math.sqrt(128)
+    errs, n = [], 0
     for b in range(4):
-        assert torch.all(o[b, :, int(L[b]):] == 0)
+        n_b = int(L[b])
+        ref = oracle.fwd(f64(inp["q"][b:b + 1, :, :n_b]), f64(inp["k"][b:b + 1, :, :n_b]),
+                         f64(inp["v"][b:b + 1, :, :n_b]), 4096, sc)
+        got = f64(o[b:b + 1, :, :n_b])
+        assert np.all(np.isfinite(got)), "non-finite output, sequence %d" % b
+        err = np.abs(got - ref)
+        errs.append((float(err.max()), float(err.sum())))
+        n += err.size
+        assert torch.all(o[b, :, n_b:] == 0)
+        del ref, got, err
+    assert max(e[0] for e in errs) <= BF16_MAX, errs
+    assert sum(e[1] for e in errs) / n <= BF16_MEAN, errs
+    # packed layout: same kernel, other addressing, same arithmetic
+    lens = [int(x) for x in L]
+    pk = [torch.cat([inp[x][b, :, :n_b].transpose(0, 1) for b, n_b in enumerate(lens)])
+          .contiguous().to(DEV) for x in ("q", "k", "v")]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    op = torch.full_like(pk[0], float("nan"))
+    swa.swa_fwd_varlen(pk[0], pk[1], pk[2], op, 4096, swa.meta_to_device(meta, DEV), cu)
+    torch.cuda.synchronize()
+    for b, n_b in enumerate(lens):
+        seg = op[int(cu[b]):int(cu[b + 1])].transpose(0, 1)
+        assert torch.equal(seg, o[b, :, :n_b]), "packed rows differ from padded, sequence %d" % b
 
 
 # ---------------------------------------------------------------------------
@@ -216,21 +223,22 @@ def test_chunk_small(dtype, Tq):
     assert np.array_equal(f64(dev["k_cache"]), kc) and np.array_equal(f64(dev["v_cache"]), vc)
 
 
-def test_chunk_workload_two_requests():
+def test_chunk_workload_full():
     """B=8, H=32, Hkv=8, Tq=512, W=4096, p U[4096, 65536], start = p mod W:
-    all outputs of requests 0 and 5 against the oracle; every ring and state."""
+    every output of every request, every ring and the state against the
+    oracle's chunk of the whole batch."""
     inp = synth.make("chunk")
     o, dev, meta = run_chunk(inp, 4096, 128, 64)
     assert meta["keys_touched"] == 8 * 4607
-    for b in (0, 5):
-        ref_o, kc, vc, rs, cl, npos = oracle_chunk(inp, 4096, 1 / math.sqrt(128),
-                                                   bsel=slice(b, b + 1))
-        check(o[b:b + 1], ref_o, torch.bfloat16, "chunk workload b=%d" % b)
-        assert np.array_equal(f64(dev["k_cache"][b:b + 1]), kc)
-        assert np.array_equal(f64(dev["v_cache"][b:b + 1]), vc)
+    ref_o, kc, vc, rs, cl, npos = oracle_chunk(inp, 4096, 1 / math.sqrt(128))
+    check(o, ref_o, torch.bfloat16, "chunk workload")
+    assert np.array_equal(f64(dev["k_cache"]), kc)
+    assert np.array_equal(f64(dev["v_cache"]), vc)
+    assert np.array_equal(dev["ring_start"].cpu().numpy(), rs)
+    assert np.array_equal(dev["cache_len"].cpu().numpy(), cl)
+    assert np.array_equal(dev["next_pos"].cpu().numpy(), npos)
     p = inp["next_pos"].numpy()
-    assert np.array_equal(dev["next_pos"].cpu().numpy(), p + 512)
-    assert np.array_equal(dev["ring_start"].cpu().numpy(), (p + 512) % 4096)
+    assert np.array_equal(npos, p + 512) and np.array_equal(rs, (p + 512) % 4096)
 
 
 # ---------------------------------------------------------------------------
