@@ -46,7 +46,7 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
            "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
            "swa_fwd_varlen", "swa_bwd_varlen", "swa_layer_plan", "swa_cache_bytes",
-           "swa_last_error")
+           "swa_last_error", "swa_decode_noalloc")
 
 
 class SwaError(RuntimeError):
@@ -91,6 +91,8 @@ def lib():
             L.swa_decode_workspace_size.restype = ctypes.c_size_t
             L.swa_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, F, P]
+            L.swa_decode_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
+                                             P, F, P]
             L.swa_layer_plan.argtypes = [I, I, I, I, P, P, P]
             L.swa_cache_bytes.argtypes = [I, I, I, I, ctypes.c_int64, I, P, P]
             L.swa_last_error.argtypes = []
@@ -433,4 +435,32 @@ def swa_decode(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_po
                             _dptr(cache_len), _dptr(next_pos), _dptr(o), _dptr(workspace),
                             ctypes.c_size_t(ws_bytes), ctypes.c_float(scale),
                             _stream(q, stream)))
+    return o
+
+
+def swa_decode_noalloc(q, k_new, v_new, k_cache, v_cache, ring_start, cache_len, next_pos, o,
+                       W, scale=None, stream=None, n_sink=0, sink_k=None, sink_v=None):
+    """swa_decode without a workspace: the library's own scratch array holds
+    the partials (for callers that cannot allocate).  Runs on q's device."""
+    for t in (q, k_new, v_new, k_cache, v_cache, o, ring_start, cache_len, next_pos):
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    B, H, d = q.shape
+    Hkv = k_new.shape[1]
+    _require(tuple(k_cache.shape) == (B, Hkv, W, d) and tuple(v_cache.shape) == (B, Hkv, W, d),
+             "cache shape must be [B,Hkv,W,d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if n_sink:
+        _require(sink_k is not None and sink_v is not None and
+                 tuple(sink_k.shape) == (B, Hkv, n_sink, d) and
+                 tuple(sink_v.shape) == (B, Hkv, n_sink, d) and sink_k.is_contiguous() and
+                 sink_v.is_contiguous(), "sink caches must be contiguous [B,Hkv,n_sink,d]")
+    import torch
+    with torch.cuda.device(q.device):
+        _check(lib().swa_decode_noalloc(_dtype_code(q), B, H, Hkv, d, W, n_sink,
+                                        _dptr(sink_k if n_sink else None),
+                                        _dptr(sink_v if n_sink else None), _dptr(q),
+                                        _dptr(k_new), _dptr(v_new), _dptr(k_cache),
+                                        _dptr(v_cache), _dptr(ring_start), _dptr(cache_len),
+                                        _dptr(next_pos), _dptr(o), ctypes.c_float(scale),
+                                        _stream(q, stream)))
     return o

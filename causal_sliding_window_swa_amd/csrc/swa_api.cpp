@@ -328,13 +328,13 @@ extern "C" size_t swa_decode_workspace_size(int B, int H, int d, int W) {
     return (size_t)B * H * swa::decode_max_splits(W) * (size_t)(d + 2) * sizeof(float);
 }
 
-extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
-                          void *sink_k, void *sink_v, const void *q,
-                          const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                          int32_t *ring_start_dev, int32_t *cache_len_dev,
-                          int32_t *next_pos_dev, void *o, void *workspace, size_t ws_bytes,
-                          float scale, void *stream) {
-    static const char *fn = "swa_decode";
+// Shared by swa_decode (caller's workspace) and swa_decode_noalloc (the
+// library's scratch array; workspace == NULL there).
+static int decode_call(const char *fn, bool noalloc, swa_dtype dt, int B, int H, int Hkv, int d,
+                       int W, int n_sink, void *sink_k, void *sink_v, const void *q,
+                       const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
+                       void *o, void *workspace, size_t ws_bytes, float scale, void *stream) {
     swa::clear_error();
     int rc;
     if ((rc = check_heads(fn, B, H, Hkv, d, W))) return rc;
@@ -366,11 +366,48 @@ extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
     if (dt == SWA_F32) return launched(fn, swa::launch_decode_f32(a, s));
+    a.n_split = swa::decode_bf16_splits(B, Hkv, W);
+    if (noalloc) {
+        // the ranges' partials go to the library's scratch array: fewer ranges
+        // when those of swa_decode would not fit (one range without sinks
+        // writes O directly and needs none)
+        const size_t per_range = (size_t)B * H * (size_t)(d + 2) * sizeof(float);
+        while (a.n_split > 1 && per_range * a.n_split > swa::kDecodeScratchBytes) a.n_split >>= 1;
+        if ((a.n_split > 1 || n_sink > 0) && per_range * a.n_split > swa::kDecodeScratchBytes)
+            return fail(SWA_EINVAL,
+                        "%s: B*H*(d+2)*4 = %zu bytes of partials exceed the %zu-byte scratch "
+                        "(with attention sinks one range needs them)", fn, per_range,
+                        swa::kDecodeScratchBytes);
+        float *scr = nullptr;
+        if ((rc = swa::decode_scratch(&scr))) return rc;
+        a.ws = scr;
+        return launched(fn, swa::launch_decode_bf16(a, s));
+    }
     const size_t need = swa_decode_workspace_size(B, H, d, W);
     if (!workspace || !aligned16(workspace) || ws_bytes < need)
         return fail(SWA_EINVAL, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu",
                     fn, need, ws_bytes);
     a.ws = (float *)workspace;
-    a.n_split = swa::decode_bf16_splits(B, Hkv, W);
     return launched(fn, swa::launch_decode_bf16(a, s));
+}
+
+extern "C" int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
+                          void *sink_k, void *sink_v, const void *q,
+                          const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                          int32_t *ring_start_dev, int32_t *cache_len_dev,
+                          int32_t *next_pos_dev, void *o, void *workspace, size_t ws_bytes,
+                          float scale, void *stream) {
+    return decode_call("swa_decode", false, dt, B, H, Hkv, d, W, n_sink, sink_k, sink_v, q,
+                       k_new, v_new, k_cache, v_cache, ring_start_dev, cache_len_dev,
+                       next_pos_dev, o, workspace, ws_bytes, scale, stream);
+}
+
+extern "C" int swa_decode_noalloc(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
+                                  void *sink_k, void *sink_v, const void *q, const void *k_new,
+                                  const void *v_new, void *k_cache, void *v_cache,
+                                  int32_t *ring_start_dev, int32_t *cache_len_dev,
+                                  int32_t *next_pos_dev, void *o, float scale, void *stream) {
+    return decode_call("swa_decode_noalloc", true, dt, B, H, Hkv, d, W, n_sink, sink_k, sink_v,
+                       q, k_new, v_new, k_cache, v_cache, ring_start_dev, cache_len_dev,
+                       next_pos_dev, o, nullptr, 0, scale, stream);
 }

@@ -27,6 +27,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
+#include "../../include/swa.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -480,6 +483,37 @@ int decode_bf16_splits(int B, int Hkv, int W) {
     int n = 1;
     while (pairs * n < 8192 && n < cap) n <<= 1;
     return n;
+}
+
+// Partials of swa_decode_noalloc: each GPU holds its own copy of this array.
+// Host code must not pass the array's name to a kernel (on the host it names
+// a stand-in, not device memory): decode_scratch() looks up the current
+// device's address once and every launch uses that.  Nothing in it needs to
+// start at zero (each range writes its partial before the merge reads it).
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+int decode_scratch(float **ptr) {
+    constexpr int MAXDEV = 64;
+    static std::mutex mu;
+    static float *addr[MAXDEV];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(SWA_EHIP, "swa_decode_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAXDEV)
+        return fail(SWA_EUNSUPPORTED, "swa_decode_noalloc: device %d beyond the %d supported",
+                    dev, MAXDEV);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SWA_EHIP, "swa_decode_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                        hipGetErrorString(e));
+        addr[dev] = (float *)p;
+    }
+    *ptr = addr[dev];
+    return SWA_OK;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {

@@ -68,6 +68,11 @@ hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 int decode_bf16_splits(int B, int Hkv, int W);
 int decode_max_splits(int W);
+// Scratch array of swa_decode_noalloc (a file-scope __device__ array in
+// swa_decode_bf16.hip, one per GPU, held until the process ends) and the
+// current device's address of it, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+int decode_scratch(float **ptr);
 // Backward of the full-sequence forward (swa_bwd.hip).
 struct BwdArgs {
     int B, H, Hkv, N, d, W, tile_q, tile_k;

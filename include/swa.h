@@ -280,6 +280,29 @@ int swa_decode(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
                int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
                void *o, void *workspace, size_t ws_bytes, float scale, void *stream);
 
+/* Allocation-free variant of swa_decode, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Arguments and results are those of swa_decode
+ * without the workspace: the bf16 path keeps its per-range partials in a
+ * scratch array inside the library, 32 MiB on each GPU it runs on (held until
+ * the process ends), at the current device's address of it, so the stream
+ * must belong to the current device.  It uses swa_decode's number of W ranges
+ * when their partials (B * H * ranges * (d + 2) * 4 bytes) fit, else halves
+ * it until they do; one range without attention sinks writes O directly and
+ * needs none.  Nothing in the scratch needs clearing (each range writes its
+ * partial before the merge reads it).  Calls that overlap on one GPU (other
+ * streams, other threads) share that scratch and race; calls ordered on one
+ * stream do not.  The fp32 path needs no scratch.
+ * Errors: as swa_decode, plus SWA_EINVAL when one range's partials do not fit
+ * (only with n_sink > 0 and B * H * (d + 2) * 4 > 32 MiB), SWA_EHIP when the
+ * scratch's address cannot be looked up. */
+int swa_decode_noalloc(swa_dtype dt, int B, int H, int Hkv, int d, int W, int n_sink,
+                       void *sink_k, void *sink_v,
+                       const void *q, const void *k_new, const void *v_new,
+                       void *k_cache, void *v_cache,
+                       int32_t *ring_start_dev, int32_t *cache_len_dev, int32_t *next_pos_dev,
+                       void *o, float scale, void *stream);
+
 /* Which layers of a stack use the window ("LLMs from scratch, chapter 10:
  * SWA and DSA", §10.2: a local:global ratio has to be resolved into whole
  * layers; a stride option picks the windowed layers).  Host only.

@@ -190,6 +190,27 @@ def test_decode_validation_codes():
     assert swa.swa_decode_workspace_size(0, 32, 128, 4096) == 0
 
 
+def _decode_noalloc(B=2, H=32, Hkv=8, d=128, W=4096, dt=0, sink=0, sink_ptr=16):
+    p = ctypes.c_void_p(16)
+    sp = ctypes.c_void_p(sink_ptr) if sink_ptr else None
+    return swa.lib().swa_decode_noalloc(dt, B, H, Hkv, d, W, sink, sp, sp, p, p, p, p, p, p, p,
+                                        p, p, ctypes.c_float(0.1), None)
+
+
+def test_decode_noalloc_validation_codes():
+    """The allocation-free decode checks what swa_decode checks, and refuses
+    shapes whose one-range partials exceed its 32 MiB scratch (only with
+    attention sinks), all before touching the device."""
+    assert _decode_noalloc(W=0) == swa.SWA_EINVAL
+    assert _decode_noalloc(H=48, Hkv=3) == swa.SWA_EUNSUPPORTED
+    assert _decode_noalloc(d=80) == swa.SWA_EUNSUPPORTED
+    assert _decode_noalloc(sink=-1) == swa.SWA_EINVAL
+    assert _decode_noalloc(sink=4, sink_ptr=0) == swa.SWA_EINVAL
+    # 1024 * 64 * (128 + 2) * 4 bytes > 32 MiB
+    assert _decode_noalloc(B=1024, H=64, Hkv=8, sink=4) == swa.SWA_EINVAL
+    assert b"scratch" in swa.lib().swa_last_error()
+
+
 def test_bf16_span_limit():
     """The bf16 tile kernels address one head's K/V rows with 32-bit offsets:
     longer spans are refused before any launch (no device memory needed)."""
