@@ -361,19 +361,17 @@ void tile_kernel(AttnArgs a) {
         }
 
         // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries;
-        // masked scores become -inf
+        // masked scores become -inf; each chain starts from an inline zero
+        // accumulator (no vector instructions to clear it)
         f32x16 sacc[2];
         auto scores = [&]() {
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int e2 = 0; e2 < 16; e2++) sacc[kb][e2] = 0.f;
             auto qk_step = [&](int kb, int ks) {
                 const int r = kb * 32 + kr_row;
                 const int c = (2 * ks + hh) ^ kswz(r);
                 const bf16x8 af =
                     __builtin_bit_cast(bf16x8, *(const u32x4 *)(ksm + r * ROWB + c * 16));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    af, qf[ks], ks == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
             };
             if (live[0] && live[1]) {
                 // all K fragments of key block 0 first, then its MFMAs while the
@@ -387,8 +385,8 @@ void tile_kernel(AttnArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
-                    sacc[0] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
+                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        kf[ks], qf[ks], ks == 0 ? f32x16{} : sacc[0], 0, 0, 0);
                     const int r = 32 + kr_row;
                     const int c = (2 * ks + hh) ^ kswz(r);
                     kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksm + r * ROWB + c * 16));
@@ -396,14 +394,18 @@ void tile_kernel(AttnArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++)
-                    sacc[1] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[1], 0, 0, 0);
+                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        kf[ks], qf[ks], ks == 0 ? f32x16{} : sacc[1], 0, 0, 0);
             } else if (live[0]) {
+                // one half skipped: its scores only need to be finite (they are
+                // masked, the tile being partial)
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(0, ks);
+                sacc[1] = f32x16{};
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(1, ks);
+                sacc[0] = f32x16{};
             }
             if (partial) {
                 // key k is visible iff (unsigned)(k - a) <= b - a; an empty interval
