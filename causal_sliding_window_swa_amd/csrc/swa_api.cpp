@@ -3,27 +3,9 @@
 // before anything is enqueued.
 #include <hip/hip_runtime.h>
 #include <limits.h>
-#include <stdarg.h>
-#include <stdio.h>
 
 #include "../../include/swa.h"
 #include "swa_internal.h"
-
-namespace swa {
-
-static thread_local char g_err[512];
-
-int fail(int code, const char *fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_err, sizeof(g_err), fmt, ap);
-    va_end(ap);
-    return code;
-}
-
-void clear_error() { g_err[0] = 0; }
-
-}  // namespace swa
 
 namespace {
 
@@ -87,8 +69,6 @@ int launched(const char *fn, hipError_t e) {
 }
 
 }  // namespace
-
-extern "C" const char *swa_last_error(void) { return swa::g_err; }
 
 extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink,
                        int tile_q, int tile_k, const void *q, const void *k, const void *v, void *o,
