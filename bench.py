@@ -329,6 +329,38 @@ def main():
         out["chunk"] = dict(wall_ms=w4, kernel_ms=e4, flops=4.0 * d4 * m4["valid_pairs"] * H4,
                             keys_touched_per_request=m4["keys_touched"] // B4)
         log("chunk: wall %.3f ms, event %.3f ms" % (w4, e4))
+        # a real stream of chunk steps: the ring moves every step, so the
+        # block metadata is rebuilt before each one (the figure above resets
+        # the ring state to reuse one build).  (a) on the device, in stream
+        # order, from the device ring state; (b) on the host, from a copy of
+        # the ring state, then copied to the device
+        for x in state0:
+            dv[x].copy_(state0[x])
+        mdev = swa.chunk_meta_buffers(B4, Tq, W4, tq, tk, dev, stats=False)
+
+        def f4d():
+            swa.swa_chunk_blockmask_dev(mdev, dv["ring_start"], dv["cache_len"], dv["next_pos"])
+            swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                  dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                  dv["next_pos"], o4, W4, mdev)
+        w4d, e4d, _ = timed(f4d, max(5, K // 5), 2)
+        out["chunk_stream_dev"] = dict(wall_ms=w4d, kernel_ms=e4d)
+        log("chunk stream, device metadata: wall %.3f ms, event %.3f ms" % (w4d, e4d))
+
+        def f4h():
+            rs_h, cl_h, np_h = (dv[x].cpu().numpy() for x in ("ring_start", "cache_len",
+                                                             "next_pos"))
+            mh = swa.swa_blockmask_build(B4, Tq, Tq, W4, tq, tk, q_start=np_h, k_start=np_h,
+                                         W_ring=W4, ring_start=rs_h, cache_len=cl_h,
+                                         next_pos=np_h)
+            swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                  dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                  dv["next_pos"], o4, W4, swa.meta_to_device(mh, dev))
+        w4h, _, _ = timed(f4h, max(5, K // 5), 2, graph=False)
+        out["chunk_stream_host"] = dict(wall_ms=w4h)
+        log("chunk stream, host metadata: wall %.3f ms" % w4h)
+        for x in state0:
+            dv[x].copy_(state0[x])
         if "sink" in only:  # 4 sinks from a sink cache, far behind every window
             m4s = swa.swa_blockmask_build(B4, Tq, Tq, W4, tq, tk, q_start=p, k_start=p,
                                           W_ring=W4, ring_start=state0["ring_start"].cpu().numpy(),
@@ -377,6 +409,33 @@ def main():
                                       kv_bytes=kv_bytes + 2.0 * B5 * Hkv5 * 4 * d5 * 2)
             log("decode sink: wall %.4f ms, event %.4f ms" % (w6, e6))
         del dv
+
+    # ---------------- HBM read ceiling of this GPU -------------
+    # a plain streaming read (libswa_measure.so, measurement support only) of
+    # as many bytes as the decode step reads, at a few grid sizes; the best
+    # is the practical ceiling beside the 8 TB/s specification
+    if "decode" in only:
+        import ctypes
+        mlib = ctypes.CDLL(os.path.join(ROOT, "causal_sliding_window_swa_amd",
+                                        "libswa_measure.so"))
+        mlib.swa_measure_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        nbytes = 1 << 30
+        buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+        best = None
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            fr = lambda: mlib.swa_measure_stream_read(
+                ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
+                ctypes.c_void_p(sink.data_ptr()), blocks,
+                ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+            _, ms_r, _ = timed(fr, 20, 3)
+            gbs_r = nbytes / (ms_r * 1e-3) / 1e9
+            if best is None or gbs_r > best[1]:
+                best = (blocks, gbs_r, ms_r)
+        out["hbm_stream"] = dict(bytes=nbytes, blocks=best[0], GB_per_s=best[1], ms=best[2])
+        log("hbm stream read: %.1f GB/s (%d blocks)" % (best[1], best[0]))
+        del buf, sink
 
     # ---------------- oracle on the host cores -------------
     # the whole prefill workload in fp64, repeated until about 10 s of work
@@ -507,6 +566,15 @@ def main():
                                            "swa_decode", src_digest("swa_decode_bf16.hip")),
                                        "kernel_ms": round(dd["kernel_ms"], 5),
                                        "kernels": "split + combine"}}
+    if "hbm_stream" in out:
+        hs = out["hbm_stream"]
+        line["hbm_stream"] = {"workload": "plain streaming read of 1 GiB (one pass, 16-byte "
+                                          "loads, %d workgroups of 256)" % hs["blocks"],
+                              "GB_per_s": round(hs["GB_per_s"], 1),
+                              "pct_of_peak": round(100 * hs["GB_per_s"] / PEAK_HBM_GBS, 2)}
+        if "decode" in line:
+            line["decode"]["pct_of_stream_read"] = round(
+                100 * line["decode"]["roofline"]["achieved"] / hs["GB_per_s"], 2)
     if "prefill_sink" in out:
         ps = out["prefill_sink"]
         t = ps["flops"] / (ps["wall_ms"] * 1e-3) / 1e12
@@ -570,6 +638,18 @@ def main():
                          "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                          "ms_per_step": round(c4["wall_ms"], 4),
                          "keys_touched_per_request": c4["keys_touched_per_request"]}
+    if "chunk_stream_dev" in out:
+        c4 = out["chunk"]
+        fl = c4["flops"]
+        line["chunk_stream"] = {
+            "workload": "the chunk workload as a stream of steps (the ring advances 512 "
+                        "positions per step), block metadata rebuilt before every step",
+            "device_metadata": {"ms_per_step": round(out["chunk_stream_dev"]["wall_ms"], 4),
+                                "TFLOP_per_s": round(fl / (out["chunk_stream_dev"]["wall_ms"]
+                                                           * 1e-3) / 1e12, 2)},
+            "host_metadata": {"ms_per_step": round(out["chunk_stream_host"]["wall_ms"], 4),
+                              "TFLOP_per_s": round(fl / (out["chunk_stream_host"]["wall_ms"]
+                                                         * 1e-3) / 1e12, 2)}}
     print(json.dumps(line), flush=True)
 
 

@@ -46,7 +46,7 @@ STAT_NAMES = ("valid_pairs", "covered_coords", "keys_touched", "n_live", "n_full
 EXPORTS = ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd", "swa_prefill_chunk",
            "swa_decode_workspace_size", "swa_decode", "swa_bwd_workspace_size", "swa_bwd",
            "swa_fwd_varlen", "swa_bwd_varlen", "swa_layer_plan", "swa_cache_bytes",
-           "swa_last_error", "swa_decode_noalloc")
+           "swa_last_error", "swa_decode_noalloc", "swa_chunk_blockmask_dev")
 
 
 class SwaError(RuntimeError):
@@ -93,13 +93,14 @@ def lib():
                                      ctypes.c_size_t, F, P]
             L.swa_decode_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
                                              P, F, P]
+            L.swa_chunk_blockmask_dev.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
             L.swa_layer_plan.argtypes = [I, I, I, I, P, P, P]
             L.swa_cache_bytes.argtypes = [I, I, I, I, ctypes.c_int64, I, P, P]
             L.swa_last_error.argtypes = []
             L.swa_last_error.restype = ctypes.c_char_p
             for n in ("swa_blockmask_size", "swa_blockmask_build", "swa_fwd",
                       "swa_prefill_chunk", "swa_decode", "swa_bwd", "swa_fwd_varlen",
-                      "swa_bwd_varlen",
+                      "swa_bwd_varlen", "swa_decode_noalloc", "swa_chunk_blockmask_dev",
                       "swa_layer_plan", "swa_cache_bytes"):
                 getattr(L, n).restype = ctypes.c_int
             _lib = L
@@ -162,6 +163,40 @@ def swa_blockmask_build(B, nq, nk_lin, W, tile_q, tile_k, q_start=None, k_start=
            "B": B, "nq": nq, "nk_lin": nk_lin, "W": W, "W_ring": W_ring}
     out.update({n: int(getattr(st, n)) for n in STAT_NAMES})
     return out
+
+
+def chunk_meta_buffers(B, Tq, W, tile_q, tile_k, device, n_sink=0, stats=True):
+    """Device arrays for swa_chunk_blockmask_dev of these shapes (allocated once,
+    rebuilt in place every step), as a metadata dict swa_prefill_chunk takes;
+    stats=False: no statistics (one kernel fewer per build)."""
+    import torch
+    ns = -(-n_sink // tile_k) * tile_k if n_sink > 0 else 0
+    nk = ns + W + Tq
+    cls_n, max_nnz = swa_blockmask_size(B, Tq, nk, tile_q, tile_k)
+    nqt = -(-Tq // tile_q)
+    dev = torch.device(device)
+    return {"row_ptr": torch.zeros(B * nqt + 1, dtype=torch.int32, device=dev),
+            "col": torch.zeros(max(1, max_nnz), dtype=torch.int32, device=dev),
+            "col_cls": torch.zeros(max(1, max_nnz), dtype=torch.uint8, device=dev),
+            "cls": torch.zeros(max(1, cls_n), dtype=torch.uint8, device=dev),
+            "stats": torch.zeros(6, dtype=torch.int64, device=dev) if stats else None,
+            "tile_q": tile_q, "tile_k": tile_k, "n_sink": n_sink, "max_len": Tq,
+            "B": B, "nq": Tq, "nk_lin": Tq, "W": W, "W_ring": W}
+
+
+def swa_chunk_blockmask_dev(meta, ring_start, cache_len, next_pos, stream=None):
+    """Rebuild, on the device and in stream order, the metadata of the next
+    swa_prefill_chunk step from the device ring state (int32 [B] tensors);
+    `meta` comes from chunk_meta_buffers and is filled in place."""
+    for t in (ring_start, cache_len, next_pos):
+        _require(t.is_contiguous() and t.numel() == meta["B"], "ring state must be int32 [B]")
+    _check(lib().swa_chunk_blockmask_dev(meta["B"], meta["nq"], meta["W"], meta["n_sink"],
+                                         meta["tile_q"], meta["tile_k"], _dptr(ring_start),
+                                         _dptr(cache_len), _dptr(next_pos), _dptr(meta["cls"]),
+                                         _dptr(meta["row_ptr"]), _dptr(meta["col"]),
+                                         _dptr(meta["col_cls"]), _dptr(meta["stats"]),
+                                         _stream(ring_start, stream)))
+    return meta
 
 
 def swa_layer_plan(L, ratio, W):

@@ -308,6 +308,37 @@ extern "C" size_t swa_decode_workspace_size(int B, int H, int d, int W) {
     return (size_t)B * H * swa::decode_max_splits(W) * (size_t)(d + 2) * sizeof(float);
 }
 
+extern "C" int swa_chunk_blockmask_dev(int B, int Tq, int W, int n_sink, int tile_q, int tile_k,
+                                       const int32_t *ring_start_dev,
+                                       const int32_t *cache_len_dev,
+                                       const int32_t *next_pos_dev, uint8_t *cls_dev,
+                                       int32_t *row_ptr_dev, int32_t *col_dev,
+                                       uint8_t *col_cls_dev, int64_t *stats_dev, void *stream) {
+    static const char *fn = "swa_chunk_blockmask_dev";
+    swa::clear_error();
+    if (W < 1) return fail(SWA_EINVAL, "%s: window W=%d must be >= 1", fn, W);
+    if (B < 1 || Tq < 1 || tile_q < 1 || tile_k < 1)
+        return fail(SWA_EINVAL, "%s: need B, Tq, tiles >= 1 (B=%d Tq=%d tile_q=%d tile_k=%d)",
+                    fn, B, Tq, tile_q, tile_k);
+    if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
+    if (W % tile_k != 0)
+        return fail(SWA_EINVAL, "%s: W=%d must be a multiple of tile_k=%d", fn, W, tile_k);
+    const long long NS = n_sink > 0 ? ((long long)n_sink + tile_k - 1) / tile_k * tile_k : 0;
+    const long long nk = NS + W + Tq;
+    const long long nqt = (Tq + tile_q - 1) / tile_q, nkt = (nk + tile_k - 1) / tile_k;
+    if (nk > INT_MAX || (long long)B * nqt * nkt > INT_MAX)
+        return fail(SWA_EINVAL, "%s: key axis or block grid too large", fn);
+    if (!ring_start_dev || !cache_len_dev || !next_pos_dev || !cls_dev || !row_ptr_dev ||
+        !col_dev || !col_cls_dev)
+        return fail(SWA_EINVAL, "%s: ring state and output arrays are required", fn);
+    swa::ChunkMetaArgs a = {};
+    a.B = B; a.Tq = Tq; a.W = W; a.n_sink = n_sink; a.tile_q = tile_q; a.tile_k = tile_k;
+    a.ring_start = ring_start_dev; a.cache_len = cache_len_dev; a.next_pos = next_pos_dev;
+    a.cls = cls_dev; a.row_ptr = row_ptr_dev; a.col = col_dev; a.col_cls = col_cls_dev;
+    a.stats = stats_dev;
+    return launched(fn, swa::launch_chunk_meta(a, (hipStream_t)stream));
+}
+
 // Shared by swa_decode (caller's workspace) and swa_decode_noalloc (the
 // library's scratch array; workspace == NULL there).
 static int decode_call(const char *fn, bool noalloc, swa_dtype dt, int B, int H, int Hkv, int d,

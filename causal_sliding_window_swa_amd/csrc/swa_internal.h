@@ -96,6 +96,19 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 bool bwd_bf16_supported(const BwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 
+// Block metadata of a chunked-prefill step built on the device from the
+// device ring state (swa_chunk_meta.hip); same arrays and statistics as
+// swa_blockmask_build for that step.
+struct ChunkMetaArgs {
+    int B, Tq, W, n_sink, tile_q, tile_k;
+    const int32_t *ring_start, *cache_len, *next_pos;
+    uint8_t *cls;
+    int32_t *row_ptr, *col;
+    uint8_t *col_cls;
+    int64_t *stats;  // may be null: the six swa_mask_stats fields
+};
+hipError_t launch_chunk_meta(const ChunkMetaArgs &a, hipStream_t s);
+
 // Ring bookkeeping (swa_ring.hip): write the new rows into their slots, then
 // advance the state; launch_commit does both (after a chunk's attention).
 hipError_t launch_ring_write(const CommitArgs &a, hipStream_t s);

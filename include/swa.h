@@ -252,6 +252,30 @@ int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, int d, int W,
                       const uint8_t *col_cls_dev,
                       void *o, float scale, void *stream);
 
+/* Block metadata of one swa_prefill_chunk step, built on the device from the
+ * ring state in device memory [M003 §07: a pattern that moves with the input
+ * is rebuilt each step, and that cost counts], so that consecutive chunk
+ * steps chain on one stream with no host copy of the ring state.  Enqueued on
+ * `stream`; it reads ring_start_dev, cache_len_dev, next_pos_dev as they are
+ * when it runs (after earlier work on the stream), so enqueue it before each
+ * swa_prefill_chunk of the same (B, Tq, W, n_sink, tile_q, tile_k).
+ * Outputs (device memory, caller-owned, sizes as swa_blockmask_size with
+ * nq = Tq and nk = NS + W + Tq, NS = n_sink rounded up to tile_k): cls_dev
+ * [B][nqt][nkt], row_ptr_dev [B*nqt+1], col_dev and col_cls_dev [max_nnz];
+ * stats_dev: NULL or device int64[6] in swa_mask_stats order.  The arrays
+ * equal those swa_blockmask_build writes for that step (nq = nk_lin = Tq,
+ * q_start = k_start = next_pos, k_len = NULL, W_ring = W, the same n_sink).
+ * The ring state must be one swa_blockmask_build accepts (ring_start in
+ * [0, W), cache_len in [0, W], next_pos >= cache_len, positions within int32);
+ * it is not re-checked on the device.
+ * Errors: SWA_EINVAL for W < 1, B, Tq or a tile < 1, n_sink < 0,
+ * W % tile_k != 0, a grid beyond int32, NULL arrays; SWA_EHIP. */
+int swa_chunk_blockmask_dev(int B, int Tq, int W, int n_sink, int tile_q, int tile_k,
+                            const int32_t *ring_start_dev, const int32_t *cache_len_dev,
+                            const int32_t *next_pos_dev, uint8_t *cls_dev, int32_t *row_ptr_dev,
+                            int32_t *col_dev, uint8_t *col_cls_dev, int64_t *stats_dev,
+                            void *stream);
+
 /* Bytes of device workspace swa_decode needs for these shapes. */
 size_t swa_decode_workspace_size(int B, int H, int d, int W);
 

@@ -284,3 +284,22 @@ def test_binding_rejects_mismatched_metadata():
     bad = {x: meta[x] for x in ("row_ptr", "col", "col_cls", "cls", "tile_q", "tile_k")}
     with pytest.raises(swa.SwaError, match="lacks"):
         swa.swa_fwd(q, k, k.clone(), q.clone(), 16, bad)
+
+
+def test_chunk_blockmask_dev_validation_codes():
+    """The device metadata builder checks its arguments before touching the
+    device (no GPU needed for these)."""
+    L = swa.lib()
+    p = ctypes.c_void_p(16)
+
+    def call(B=2, Tq=64, W=256, S=0, tq=128, tk=64, ptr=p):
+        return L.swa_chunk_blockmask_dev(B, Tq, W, S, tq, tk, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                         None, None)
+    assert call(W=0) == swa.SWA_EINVAL
+    assert call(B=0) == swa.SWA_EINVAL
+    assert call(Tq=0) == swa.SWA_EINVAL
+    assert call(tk=0) == swa.SWA_EINVAL
+    assert call(S=-1) == swa.SWA_EINVAL
+    assert call(W=96) == swa.SWA_EINVAL  # W not a multiple of tile_k
+    assert call(ptr=None) == swa.SWA_EINVAL
+    assert call(B=65535, Tq=1 << 20, W=1 << 20, tq=1, tk=1) == swa.SWA_EINVAL  # grid beyond int32
