@@ -424,7 +424,7 @@ def main():
         buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
         sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
         best = None
-        for blocks in (1024, 2048, 4096, 8192, 16384):
+        for blocks in (2048, 8192, 16384, 32768, 65536):
             fr = lambda: mlib.swa_measure_stream_read(
                 ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
                 ctypes.c_void_p(sink.data_ptr()), blocks,
