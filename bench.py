@@ -209,6 +209,13 @@ def main():
         prefill["tile64"] = dict(wall_ms=w64, kernel_ms=e64, n_live=m64["n_live"],
                                  covered=m64["covered_coords"])
         log("prefill tile 64: graph %.4f ms/step, event %.4f ms" % (w64, e64))
+        # 128-key tiles (streamed as 64-key halves): half the metadata entries
+        m128 = swa.swa_blockmask_build(B, N, N, W, 128, 128)
+        md128 = swa.meta_to_device(m128, dev)
+        w128, e128, _ = timed(lambda: swa.swa_fwd(q, k, v, o, W, md128), K, WU)
+        prefill["tile128"] = dict(wall_ms=w128, kernel_ms=e128, n_live=m128["n_live"],
+                                  covered=m128["covered_coords"])
+        log("prefill tiles 128x128: graph %.4f ms/step, event %.4f ms" % (w128, e128))
         # cold caches: 1 GiB written between launches evicts L2 and the
         # 256 MB Infinity Cache; only the kernel is inside the events
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -230,7 +237,7 @@ def main():
         _, eden, _ = timed(lambda: swa.swa_fwd(q, k, v, o, N, mdd), max(3, K // 10), 2)
         prefill["dense"] = dict(kernel_ms=eden, valid_pairs=mden["valid_pairs"])
         log("prefill at W=N: event %.4f ms" % eden)
-        del mdd, md64
+        del mdd, md64, md128
 
     # ---------------- backward on the prefill workload -------------
     if "bwd" in only:
@@ -536,6 +543,16 @@ def main():
             "kernel_TFLOP_per_s": round(pf["flops"] / (t64["kernel_ms"] * 1e-3) / 1e12, 2),
             "ms_per_step": round(t64["wall_ms"], 5),
             "useful_fraction_of_covered": round(pf["stats"]["valid_pairs"] / t64["covered"], 4)}
+    if "tile128" in pf:
+        t128 = pf["tile128"]
+        line["prefill_tile128"] = {
+            "workload": "prefill workload with 128x128 tiles (%d live tiles, each streamed as "
+                        "two 64-key halves)" % t128["n_live"],
+            "TFLOP_per_s": round(pf["flops"] / (t128["wall_ms"] * 1e-3) / 1e12, 2),
+            "kernel_TFLOP_per_s": round(pf["flops"] / (t128["kernel_ms"] * 1e-3) / 1e12, 2),
+            "ms_per_step": round(t128["wall_ms"], 5),
+            "useful_fraction_of_covered": round(pf["stats"]["valid_pairs"] / t128["covered"],
+                                                4)}
     if "cold" in pf:
         line["prefill_cold_caches"] = {
             "workload": "prefill workload, 1 GiB written between launches (L2 and Infinity "

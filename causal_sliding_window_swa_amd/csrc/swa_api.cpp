@@ -57,10 +57,18 @@ int check_span(const char *fn, swa_dtype dt, long long rows, long long row_bytes
 int check_tiles(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
     if (tile_q < 1 || tile_k < 1)
         return fail(SWA_EINVAL, "%s: tiles must be >= 1 (%d, %d)", fn, tile_q, tile_k);
-    if (dt == SWA_BF16 && !((tile_q == 128 || tile_q == 64) && tile_k == 64))
-        return fail(SWA_EUNSUPPORTED, "%s: bf16 kernels take (tile_q, tile_k) = (128, 64) or "
-                    "(64, 64), got (%d, %d)", fn, tile_q, tile_k);
+    if (dt == SWA_BF16 && !((tile_q == 128 || tile_q == 64) && (tile_k == 64 || tile_k == 128)))
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 kernels take tile_q in {64, 128} and tile_k in "
+                    "{64, 128}, got (%d, %d)", fn, tile_q, tile_k);
     return SWA_OK;
+}
+
+// the MFMA backward kernels take 64-key tiles only
+int check_tiles_bwd(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
+    int rc = check_tiles(fn, dt, tile_q, tile_k);
+    if (rc == SWA_OK && dt == SWA_BF16 && tile_k != 64)
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 backward takes tile_k = 64, got %d", fn, tile_k);
+    return rc;
 }
 
 int launched(const char *fn, hipError_t e) {
@@ -211,7 +219,7 @@ extern "C" int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
                     total, max_len);
     if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_tiles_bwd(fn, dt, tile_q, tile_k))) return rc;
     // query-side rows are H * d elements apart (the wider of the two strides)
     if ((rc = check_span(fn, dt, max_len, 2LL * d * H))) return rc;
     const void *ptrs[] = {q, k, v, o, dout, lse_dev, dq, dk, dv, workspace, row_ptr_dev, col_dev};

@@ -8,7 +8,9 @@
 // query tile and visits only the key tiles its metadata row lists; only
 // partial tiles are masked per element.
 //
-// Work split (tile_q = 32 * NW query rows, tile_k = 64 keys, head dim D):
+// Work split (tile_q = 32 * NW query rows, head dim D; K/V staged 64 keys at a
+// time; the metadata's key tile is 64 keys, or 128 keys streamed as two
+// 64-key halves):
 //   * one workgroup per (query tile, head, batch).  In the logical order the
 //     query heads of one KV group are next to each other (they read identical
 //     K/V tiles) and then the query tiles (neighbours share most of theirs);
@@ -115,7 +117,7 @@ __device__ __forceinline__ int xcd_deal(int p, int T) {
     return Tm + xcd_remap(p - Tm, T - Tm);
 }
 
-template <int MODE, int D, int NW, bool PK>
+template <int MODE, int D, int NW, bool PK, int SUB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tile_kernel(AttnArgs a) {
     constexpr int KS = D / 16;          // k-steps of the QK product
@@ -146,11 +148,15 @@ void tile_kernel(AttnArgs a) {
     const int b = L / (G * nqt * a.Hkv);
     const int h = g * G + h_in;
 
+    // SUB = 64-key halves per metadata tile (tile_k 64 or 128); key tiles
+    // below are counted in 64-key units
+    constexpr int sub = SUB;
     KeyPos kp;
     kp.nq = nq;
     kp.W = a.W;
-    // chunk key axis: [sink tiles (with sinks) | ring tiles | new rows]
-    kp.nst = (MODE == 1 && a.n_sink > 0) ? (a.n_sink + BN - 1) / BN : 0;
+    // chunk key axis: [sink slots, n_sink rounded up to tile_k (with sinks) |
+    // ring tiles | new rows]
+    kp.nst = (MODE == 1 && a.n_sink > 0) ? (a.n_sink + a.tile_k - 1) / a.tile_k * sub : 0;
     kp.nrt = (MODE == 1) ? a.W / BN : 0;
     // packed batch (PK): sequence b owns tokens cu[b] .. cu[b+1]-1 of a
     // token-major [tokens][heads][D] layout; only its own rows exist
@@ -162,21 +168,6 @@ void tile_kernel(AttnArgs a) {
     kp.np = (MODE == 1) ? a.next_pos[b] : 0;
     const int qlen = kp.qlen;
     const int qbase = (MODE == 1) ? kp.np : 0;  // logical position of query row 0
-
-    // ---- this wave's 32 query rows in registers (B operand of S^T = K Q^T)
-    const int row0 = qt * 32 * NW + wave * 32;
-    const int myrow = row0 + lq;
-    bf16x8 qf[KS];
-    {
-        const __bf16 *qp = (const __bf16 *)a.q +
-                           (PK ? ((size_t)(cub + myrow) * a.H + h) * D
-                               : (((size_t)b * a.H + h) * nq + myrow) * D);
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            u32x4 x = (myrow < nrows) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
 
     // ---- key/value rows of a tile (rows past the data read as zeros through
     // the buffer range check below: finite, and always masked)
@@ -247,6 +238,35 @@ void tile_kernel(AttnArgs a) {
             load_tile(klr, vlr, (kr - kp.nrt) * BN * RSB, kdst);
     };
 
+    // The first key tile of the plain forward follows from the tile's first row
+    // (tile 0 with sinks, else the one holding row0 - W + 1), so its K/V load
+    // starts before the query rows and the metadata row are read: the
+    // metadata's first entry is checked against it below (a mismatch, which a
+    // metadata row built with another key length can give, waits for the
+    // predicted load and issues the listed tile).
+    const int row0_wg = qt * 32 * NW;
+    int pred = -1;
+    if (MODE == 0 && row0_wg < kp.qlen) {
+        const int first = a.n_sink > 0 ? 0 : max(0, row0_wg - a.W + 1);
+        pred = first / a.tile_k * sub;
+        issue(pred, stage0);
+    }
+
+    // ---- this wave's 32 query rows in registers (B operand of S^T = K Q^T)
+    const int row0 = qt * 32 * NW + wave * 32;
+    const int myrow = row0 + lq;
+    bf16x8 qf[KS];
+    {
+        const __bf16 *qp = (const __bf16 *)a.q +
+                           (PK ? ((size_t)(cub + myrow) * a.H + h) * D
+                               : (((size_t)b * a.H + h) * nq + myrow) * D);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            u32x4 x = (myrow < nrows) ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
     // ---- running softmax state: lanes l and l^32 share query column lq
     const float c2 = a.scale * LOG2E;
     float m_ref = 0.f, l_run = 0.f;  // p = exp2(s*c2 - m_ref); O, l share m_ref
@@ -284,20 +304,23 @@ void tile_kernel(AttnArgs a) {
         v_cls = a.col_cls[e0 + lz];
         v_col1 = (e0 + 1 < e1) ? a.col[e0 + 1 + lz] : 0;
     }
-    auto tile = [&](int e, const char *cur, char *nxt) {
-        const int kt = __builtin_amdgcn_readfirstlane(v_col);
-        const int kt1 = __builtin_amdgcn_readfirstlane(v_col1);
-        const int cls = __builtin_amdgcn_readfirstlane(v_cls);
+    // One 64-key step: key tile kt (64-key units) of class cls is in `cur`;
+    // the K/V of step tile ktn (none when < 0) go to `nxt`; with next_meta,
+    // the metadata of entry e + 2 (column) and e + 1 (class) is loaded.
+    auto tile = [&](int e, int kt, int cls, int ktn, bool next_meta, const char *cur,
+                    char *nxt) {
         const int kr = kt - kp.nst;  // index on the [ring | new rows] part
         const bool ragged = (kr - kp.nrt) >= nlin_full;
         const bool partial = (cls == 2) || ragged;
         __syncthreads();  // this tile is in LDS; every wave is done with the previous one
-        if (e + 1 < e1) issue(kt1, nxt);
+        if (ktn >= 0) issue(ktn, nxt);
         // loads for the next tiles (after the barrier, so that its wait does
         // not include them)
-        v_col = v_col1;
-        v_col1 = (e + 2 < e1) ? a.col[e + 2 + lz] : 0;
-        v_cls = (e + 1 < e1) ? a.col_cls[e + 1 + lz] : 0;
+        if (next_meta) {
+            v_col = v_col1;
+            v_col1 = (e + 2 < e1) ? a.col[e + 2 + lz] : 0;
+            v_cls = (e + 1 < e1) ? a.col_cls[e + 1 + lz] : 0;
+        }
         const char *ksm = cur;
         const char *vsm = cur + TILEB;
 
@@ -519,10 +542,36 @@ void tile_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_s_setprio(0);
     };
-    if (e1 > e0) issue(__builtin_amdgcn_readfirstlane(v_col), stage0);
-    for (int e = e0; e < e1; e += 2) {
-        tile(e, stage0, stage1);
-        if (e + 1 < e1) tile(e + 1, stage1, stage0);
+    {
+        const int first = (e1 > e0) ? __builtin_amdgcn_readfirstlane(v_col) * sub : -1;
+        if (first != pred) {
+            if (pred >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (first >= 0) issue(first, stage0);
+        }
+    }
+    auto meta = [&](int &kt, int &cls, int &kt1) {
+        kt = __builtin_amdgcn_readfirstlane(v_col);
+        cls = __builtin_amdgcn_readfirstlane(v_cls);
+        kt1 = __builtin_amdgcn_readfirstlane(v_col1);
+    };
+    if (SUB == 1) {
+        for (int e = e0; e < e1; e += 2) {
+            int kt, cls, kt1;
+            meta(kt, cls, kt1);
+            tile(e, kt, cls, e + 1 < e1 ? kt1 : -1, true, stage0, stage1);
+            if (e + 1 < e1) {
+                meta(kt, cls, kt1);
+                tile(e + 1, kt, cls, e + 2 < e1 ? kt1 : -1, true, stage1, stage0);
+            }
+        }
+    } else {
+        // a 128-key entry: its two halves go through the two stages in order
+        for (int e = e0; e < e1; e++) {
+            int kt, cls, kt1;
+            meta(kt, cls, kt1);
+            tile(e, 2 * kt, cls, 2 * kt + 1, false, stage0, stage1);
+            tile(e, 2 * kt + 1, cls, e + 1 < e1 ? 2 * kt1 : -1, true, stage1, stage0);
+        }
     }
 
     // ---- epilogue: O = O / l; rows without any visible key (padding) get 0.
@@ -547,28 +596,33 @@ void tile_kernel(AttnArgs a) {
     }
 }
 
-template <int MODE, int D, int NW>
+template <int MODE, int D, int NW, int SUB>
 hipError_t launch_one(const AttnArgs &a, hipStream_t s) {
     const long nqt = (a.nq + 32 * NW - 1) / (32 * NW);
     const long total = nqt * a.H * a.B;
     if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (MODE == 0 && a.cu)
-        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true>), dim3((unsigned)total), dim3(NW * 64),
-                           0, s, a);
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true, SUB>), dim3((unsigned)total),
+                           dim3(NW * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false>), dim3((unsigned)total),
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false, SUB>), dim3((unsigned)total),
                            dim3(NW * 64), 0, s, a);
     return hipGetLastError();
+}
+
+template <int MODE, int D, int NW>
+hipError_t launch_sub(const AttnArgs &a, hipStream_t s) {
+    return a.tile_k == 2 * BN ? launch_one<MODE, D, NW, 2>(a, s) : launch_one<MODE, D, NW, 1>(a, s);
 }
 
 template <int MODE>
 hipError_t launch_mode(const AttnArgs &a, hipStream_t s) {
     if (a.d == 128) {
-        if (a.tile_q == 128) return launch_one<MODE, 128, 4>(a, s);
-        return launch_one<MODE, 128, 2>(a, s);
+        if (a.tile_q == 128) return launch_sub<MODE, 128, 4>(a, s);
+        return launch_sub<MODE, 128, 2>(a, s);
     }
-    if (a.tile_q == 128) return launch_one<MODE, 64, 4>(a, s);
-    return launch_one<MODE, 64, 2>(a, s);
+    if (a.tile_q == 128) return launch_sub<MODE, 64, 4>(a, s);
+    return launch_sub<MODE, 64, 2>(a, s);
 }
 
 }  // namespace

@@ -128,9 +128,12 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q
  * with the same B, N, W, n_sink, tile_q, tile_k and lengths; only listed key tiles
  * are read, and only partial ones are masked per element.  The kernel does
  * not re-check the metadata: metadata of other shapes is a caller error.
- * Supported: SWA_BF16 with d in {64, 128}, (tile_q, tile_k) = (128, 64) or
- * (64, 64), and N * d * 2 < 2^31 (one head's K rows are addressed with 32-bit
- * offsets); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
+ * Supported: SWA_BF16 with d in {64, 128}, tile_q in {64, 128}, tile_k in
+ * {64, 128} (a 128-key tile is streamed as two 64-key halves; coarser tiles
+ * halve the metadata but can cover more masked pairs, "Weight sparsity vs
+ * attention sparsity" (AI-infra KB) §04), and N * d * 2 < 2^31 (one head's K
+ * rows are addressed with 32-bit offsets); SWA_F32 with d a multiple of 4 in
+ * [4, 128] and any tiles.
  * W >= N is legal (dense causal).
  * lse_dev: NULL, or device fp32 [B][H][N] that receives each row's natural-log
  * log-sum-exp of its visible scaled scores (-inf for rows that see no key),
@@ -207,8 +210,8 @@ int swa_bwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W, int n_sink
  * Every output row is written; no padding is read or written.  The kernels
  * do not re-check cu_seqlens against the metadata: inconsistent ones are a
  * caller error.
- * Supported: as swa_fwd_varlen for dt, d and tiles (bf16: d in {64, 128},
- * (tile_q, tile_k) = (128, 64) or (64, 64), on the MFMA kernels, with
+ * Supported: as swa_fwd_varlen for dt and d (bf16: d in {64, 128}, tile_q in
+ * {64, 128} and tile_k = 64, on the MFMA kernels, with
  * max_len * H * d * 2 < 2^31; fp32: d % 4 == 0, d <= 128, any positive tiles,
  * on the fp32-arithmetic kernels); anything else is SWA_EUNSUPPORTED.
  * Errors: SWA_EINVAL (as swa_fwd_varlen, NULL cls_dev, small workspace),

@@ -69,7 +69,8 @@ def test_fwd_validation_codes():
     assert _fwd(d=96) == swa.SWA_EUNSUPPORTED
     assert _fwd(dt=1, d=6) == swa.SWA_EUNSUPPORTED
     assert _fwd(tq=32) == swa.SWA_EUNSUPPORTED
-    assert _fwd(tk=128) == swa.SWA_EUNSUPPORTED
+    assert _fwd(tk=32) == swa.SWA_EUNSUPPORTED
+    assert _fwd(tk=256) == swa.SWA_EUNSUPPORTED
     assert _fwd(ptr=0) == swa.SWA_EINVAL
     assert _fwd(ptr=8) == swa.SWA_EINVAL  # misaligned
     assert _fwd(dt=7) == swa.SWA_EINVAL
