@@ -72,6 +72,26 @@ def counters_for(kernel_key, digest):
     return rec.get("bytes_per_launch")
 
 
+def counter_summary(name, digest):
+    """The rocprofv3 record of this kernel in profiles/counters_<name>.json
+    (kernel trace and counter passes of one run), if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    d = rec["derived"]
+    return {"record": "profiles/counters_%s.json" % name,
+            "trace_mean_ms": rec["trace"]["mean_ms"],
+            "frac_from_trace": rec["frac_of_bf16_peak_from_trace"],
+            "mfma_busy": d["mfma_busy_frac_of_simd_cycles"],
+            "valu_coexec_of_mfma_busy": d["valu_coexec_frac_of_mfma_busy"],
+            "l2_hit": d["l2_hit_frac"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -108,16 +128,20 @@ def main():
     last_events = []  # per-launch event times (ms) of the latest timed() call
 
     def timed(fn, steps, warmup, reset=None, graph=True):
-        """(ms per step, mean event-timed ms per step, eager wall ms per step).
+        """(ms per step, event-timed ms per step, eager wall ms per step).
 
-        The first figure is the wall time of one replay of a HIP graph holding
-        the `steps` steps, bracketed by device synchronisations, so that the
-        host's per-launch cost between steps is not counted.  The GPU lowers
-        its clocks within milliseconds of going idle and needs tens of
-        milliseconds of load to raise them again (graph capture and
-        instantiation leave it idle), so after the `warmup` eager steps and
-        the capture the graph is replayed, untimed, for SETTLE_S seconds
-        before the timed replay; the event-timed and eager passes follow
+        The first figure is the host wall time of one replay of a HIP graph
+        holding the `steps` steps, bracketed by device synchronisations, so
+        that the host's per-launch cost between steps is not counted; the
+        second is the same replay timed by HIP events recorded on the launch
+        stream around it (the GPU time of the timed region over `steps`,
+        which is what a kernel trace's mean duration of a one-kernel step
+        reproduces).  The GPU lowers its clocks within milliseconds of going
+        idle and needs tens of milliseconds of load to raise them again
+        (graph capture and instantiation leave it idle), so after the
+        `warmup` eager steps and the capture the graph is replayed, untimed,
+        for SETTLE_S seconds before the timed replay; a pass with one event
+        pair per step (last_events: their spread) and an eager pass follow
         while the GPU is still busy.  graph=False (steps with host work): the
         eager wall time only."""
         def step():
@@ -144,10 +168,14 @@ def main():
         while time.perf_counter() - t0 < SETTLE_S:
             g.replay()
             torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        r0.record(stream)
         g.replay()
+        r1.record(stream)
         torch.cuda.synchronize()
         gms = (time.perf_counter() - t0) * 1e3 / steps
+        region = r0.elapsed_time(r1) / steps
         del g
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
@@ -159,13 +187,12 @@ def main():
             e.record(stream)
         torch.cuda.synchronize()
         last_events[:] = sorted(s.elapsed_time(e) for s, e in evs)
-        ev = sum(last_events) / steps
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
-        return gms, ev, wall
+        return gms, region, wall
 
     out = {}
 
@@ -188,8 +215,8 @@ def main():
     fwd = lambda: swa.swa_fwd(q, k, v, o, W, md)
     wall_ms, ev_ms, eager_ms = timed(fwd, K, WU)
     ev_median, ev_min = last_events[K // 2], last_events[0]
-    log("prefill: graph %.4f ms/step, eager %.4f ms/step, event %.4f ms/launch" % (
-        wall_ms, eager_ms, ev_ms))
+    log("prefill: graph %.4f ms/step, eager %.4f ms/step, event-timed region %.4f ms/step, "
+        "per-launch events median %.4f ms" % (wall_ms, eager_ms, ev_ms, ev_median))
     # end to end with the metadata rebuilt and copied each step
     def fwd_with_meta():
         m = swa.swa_blockmask_build(B, N, N, W, tq, tk)
@@ -321,13 +348,18 @@ def main():
                                      cache_len=inp["cache_len"].numpy(), next_pos=p)
         md4 = swa.meta_to_device(m4, dev)
         dv = {x: inp[x].to(dev) for x in inp}
+        # the ring state as three rows of one tensor, so that a step's reset is
+        # one small copy
+        st3 = torch.stack([dv[x] for x in ("ring_start", "cache_len", "next_pos")]).contiguous()
+        for i, x in enumerate(("ring_start", "cache_len", "next_pos")):
+            dv[x] = st3[i]
         state0 = {x: dv[x].clone() for x in ("ring_start", "cache_len", "next_pos")}
+        st3_0 = st3.clone()
         o4 = torch.empty_like(dv["q"])
         del inp
 
         def reset4():  # same ring state each step, so the metadata stays valid
-            for x in state0:
-                dv[x].copy_(state0[x])
+            st3.copy_(st3_0)
 
         f4 = lambda: swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
                                            dv["v_cache"], dv["ring_start"], dv["cache_len"],
@@ -513,10 +545,13 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counters_for("swa_fwd_prefill", tile_digest),
-                     "kernel": "swa::tile_kernel<0,128,4> (swa_fwd)",
+                     "kernel": "swa::tile_kernel<0,128,4,false,1> (swa_fwd)",
                      "kernel_ms": round(pf["kernel_ms"], 5),
-                     "kernel_ms_median": round(pf["kernel_ms_median"], 5),
-                     "kernel_ms_min": round(pf["kernel_ms_min"], 5)},
+                     "kernel_ms_timing": "HIP events on the launch stream around the timed "
+                                         "graph replay of the K steps, divided by K",
+                     "per_launch_event_ms_median": round(pf["kernel_ms_median"], 5),
+                     "per_launch_event_ms_min": round(pf["kernel_ms_min"], 5),
+                     "counters": counter_summary("prefill", tile_digest)},
         "metadata": {"build_ms": round(pf["meta_ms"], 4), "h2d_ms": round(pf["meta_h2d_ms"], 4),
                      "e2e_ms_per_step_with_build": round(pf["e2e_ms"], 4),
                      "e2e_TFLOPs_with_build": round(pf["flops"] / (pf["e2e_ms"] * 1e-3) / 1e12,
@@ -621,7 +656,9 @@ def main():
                                            "lengths U[8192,32768]",
                                "TFLOP_per_s": round(t, 2),
                                "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
-                               "ms_per_step": round(g3["wall_ms"], 4)}
+                               "ms_per_step": round(g3["wall_ms"], 4),
+                               "kernel_ms": round(g3["kernel_ms"], 4),
+                               "useful_GFLOP": round(g3["flops"] / 1e9, 3)}
     if "gqa_packed" in out:
         gp = out["gqa_packed"]
         t = gp["flops"] / (gp["wall_ms"] * 1e-3) / 1e12
@@ -630,7 +667,9 @@ def main():
                                                   "padding)" % gp["tokens"],
                                       "TFLOP_per_s": round(t, 2),
                                       "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
-                                      "ms_per_step": round(gp["wall_ms"], 4)}
+                                      "ms_per_step": round(gp["wall_ms"], 4),
+                                      "kernel_ms": round(gp["kernel_ms"], 4),
+                                      "useful_GFLOP": round(gp["flops"] / 1e9, 3)}
     if "gqa_bwd_packed" in out:
         gb = out["gqa_bwd_packed"]
         t = gb["flops"] / (gb["wall_ms"] * 1e-3) / 1e12
@@ -654,6 +693,8 @@ def main():
                          "TFLOP_per_s": round(t, 2),
                          "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                          "ms_per_step": round(c4["wall_ms"], 4),
+                         "kernel_ms": round(c4["kernel_ms"], 4),
+                         "useful_GFLOP": round(c4["flops"] / 1e9, 3),
                          "keys_touched_per_request": c4["keys_touched_per_request"]}
     if "chunk_stream_dev" in out:
         c4 = out["chunk"]
