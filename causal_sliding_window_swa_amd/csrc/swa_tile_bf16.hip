@@ -439,7 +439,13 @@ void tile_kernel(AttnArgs a) {
                 const uint32_t n1 = x1 ? 0u : (uint32_t)(b1 - a1);
                 const uint32_t n2 = x2 ? 0u : (uint32_t)(b2 - a2);
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++)
+                for (int kb = 0; kb < 2; kb++) {
+                    // a 32-key half that every row of the wave sees whole
+                    // needs no mask (in a partial tile most halves are whole
+                    // or dead for a given wave; only the diagonal ones mix)
+                    const bool whole = (a1 <= kb * 32 && b1 >= kb * 32 + 31) ||
+                                       (two && a2 <= kb * 32 && b2 >= kb * 32 + 31);
+                    if (__ballot(!whole) == 0) continue;
 #pragma unroll
                     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -449,6 +455,7 @@ void tile_kernel(AttnArgs a) {
                                 ((uint32_t)(c - L1) <= n1) | ((uint32_t)(c - L2) <= n2);
                             sacc[kb][4 * i + j] = vis ? sacc[kb][4 * i + j] : -INFINITY;
                         }
+                }
             }
         };
         // P = exp2(S*c2 - m_ref) rounded to bf16, packed as the PV B operands
