@@ -79,10 +79,19 @@ __device__ __forceinline__ int xcd_deal(int p, int T) {
     return Tm + xcd_remap(p - Tm, T - Tm);
 }
 
-// 16-byte chunk c of row r sits at physical chunk c ^ (r % chunks per row).
+// 16-byte chunk c of row r sits at physical chunk c ^ swz(r).  The staged Q,
+// dO and K tiles are read both ways, as rows (16 lanes: 16 consecutive rows,
+// one chunk) and by transposing reads (32 lanes: 4 consecutive rows, 4
+// consecutive chunks), so the swizzle must spread both over the 64 four-byte
+// banks (256 bytes).  D = 128 (16 chunks, one row per 256 bytes): the two
+// 2-bit fields of r % 16 swapped, distinct over 16 rows and distinct in its
+// top bits over 4 rows.  D = 64 (8 chunks, two rows per 256 bytes): rows of
+// one parity get distinct values, and rows r, r + 2 differ in bit 2.  (r % 16
+// alone left the transposing reads with 4-way bank conflicts at D = 128.)
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-    return r & (CPR - 1);
+    if (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // 8 bf16 of a transposing read pair: lanes' 4-element pieces of rows

@@ -180,9 +180,13 @@ void tile_kernel(AttnArgs a) {
                                                    : kvh * (size_t)nq * D);
     const __bf16 *kring = (MODE == 1) ? (const __bf16 *)a.kc + kvh * (size_t)a.W * D : nullptr;
     const __bf16 *vring = (MODE == 1) ? (const __bf16 *)a.vc + kvh * (size_t)a.W * D : nullptr;
-    // swizzles: logical 16-byte chunk c of row r sits at physical chunk c ^ swz(r)
-    auto kswz = [](int r) { return r & (CPR - 1); };
-    auto vswz = [](int r) { return ((r & 3) << 2) & (CPR - 1); };
+    // swizzles: logical 16-byte chunk c of row r sits at physical chunk c ^ swz(r).
+    // K is read as rows (16 lanes: 16 consecutive rows, one chunk), V by
+    // transposing reads (32 lanes: 4 consecutive rows, 4 consecutive chunks);
+    // each swizzle spreads its pattern over the 64 four-byte banks.  At D = 64
+    // two rows share 256 bytes, so rows of one parity must differ.
+    auto kswz = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); };
+    auto vswz = [](int r) { return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); };
 
     // byte offsets of this lane's 16-byte pieces inside a tile (tile-invariant)
     uint32_t koff[LPW], voff[LPW];
