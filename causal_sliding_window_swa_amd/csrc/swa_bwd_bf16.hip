@@ -418,7 +418,6 @@ void dkdv_kernel(BwdArgs a) {
     const int spt = (tq + BN - 1) / BN;  // 64-row steps per query tile
     const uint8_t *clsb = a.cls + (size_t)b * nqt * nkt;
     const int qtn = qt_hi - qt_lo + 1;
-    const int nsteps = G * qtn * spt;
     // the class-grid column of this key tile over [qt_lo, qt_hi], read once
     // into two wave-wide masks (live, partial) when it spans at most 64 query
     // tiles; the step loop then never waits on a global load for it
@@ -436,22 +435,38 @@ void dkdv_kernel(BwdArgs a) {
         }
         return clsb[(size_t)qt * nkt + kt];
     };
-    auto live_from = [&](int t) __attribute__((always_inline)) -> int  {
-        for (; t < nsteps; t++) {
-            const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
-            if (cls_of(qt) != 0 && qt * tq + sub * BN < nrows) break;
-        }
-        return t;
+    // a step's position: head h of the group, query tile qt_lo + q, 64-row
+    // block s of it (s fastest, then q, then h); advanced by increments, so
+    // that the scalar code divides by nothing
+    struct Pos {
+        int h, q, s;
     };
-    auto step_rows = [&](int t, int &hq, int &s0, bool &part) __attribute__((always_inline)) {
-        const int sub = t % spt, qt = qt_lo + (t / spt) % qtn;
-        hq = g * G + t / (spt * qtn);
-        s0 = qt * tq + sub * BN;
+    auto next = [&](Pos p) __attribute__((always_inline)) -> Pos {
+        if (++p.s == spt) {
+            p.s = 0;
+            if (++p.q == qtn) {
+                p.q = 0;
+                p.h++;
+            }
+        }
+        return p;
+    };
+    auto live_from = [&](Pos p) __attribute__((always_inline)) -> Pos {
+        for (; p.h < G; p = next(p)) {
+            const int qt = qt_lo + p.q;
+            if (cls_of(qt) != 0 && qt * tq + p.s * BN < nrows) break;
+        }
+        return p;
+    };
+    auto step_rows = [&](Pos p, int &hq, int &s0, bool &part) __attribute__((always_inline)) {
+        const int qt = qt_lo + p.q;
+        hq = g * G + p.h;
+        s0 = qt * tq + p.s * BN;
         // a full class counts only in-range pairs: steps or key tiles cut by
         // the array edge are masked too
         part = cls_of(qt) == 2 || s0 + BN > nrows || kt * BN + BN > nrows;
     };
-    auto issue = [&](int t, char *dst) __attribute__((always_inline)) {
+    auto issue = [&](Pos t, char *dst) __attribute__((always_inline)) {
         int hq, s0;
         bool part;
         step_rows(t, hq, s0, part);
@@ -472,9 +487,9 @@ void dkdv_kernel(BwdArgs a) {
     const int tr_row = 4 * hh + (tr_j >> 2);
     const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (tr_j & 3);
 
-    auto step = [&](int t, const char *cur, char *nxt, int tnext) {
+    auto step = [&](Pos t, const char *cur, char *nxt, Pos tnext) {
         __syncthreads();
-        if (tnext < nsteps) issue(tnext, nxt);
+        if (tnext.h < G) issue(tnext, nxt);
         int hq, s0;
         bool part;
         step_rows(t, hq, s0, part);
@@ -621,13 +636,13 @@ void dkdv_kernel(BwdArgs a) {
             }
         }
     };
-    int t = live_from(0);
-    if (t < nsteps) issue(t, stage0);
-    while (t < nsteps) {
-        const int t1 = live_from(t + 1);
+    Pos t = live_from(Pos{0, 0, 0});
+    if (t.h < G) issue(t, stage0);
+    while (t.h < G) {
+        const Pos t1 = live_from(next(t));
         step(t, stage0, stage1, t1);
-        if (t1 >= nsteps) break;
-        const int t2 = live_from(t1 + 1);
+        if (t1.h >= G) break;
+        const Pos t2 = live_from(next(t1));
         step(t1, stage1, stage0, t2);
         t = t2;
     }
