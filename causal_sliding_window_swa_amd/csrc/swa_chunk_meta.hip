@@ -23,12 +23,12 @@
 // brute force.
 //
 // Two kernels: the first classifies every (batch, query tile, key tile), one
-// workgroup per query tile; the second, one workgroup, walks the class grid in
-// row-major order, 1024 entries per round, and a block-wide prefix count of
-// the live ones places them in the CSR arrays in ascending key tile, the
-// first entry of each row writing its row pointer.  With statistics
-// requested, a third, tiny kernel clears them first and the classifier adds
-// its sums with atomics.
+// workgroup per query tile, four lanes per key tile; the second, one workgroup,
+// walks the class grid in row-major order, 1024 entries per round, and a
+// block-wide prefix count of the live ones places them in the CSR arrays in ascending
+// key tile, the first entry of each row writing its row pointer.  With
+// statistics requested, a third, tiny kernel clears them first and the
+// classifier adds its sums with atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -120,19 +120,31 @@ __global__ __launch_bounds__(CT) void chunk_classify_kernel(ChunkMetaArgs a) {
     const int64_t np = g.np;
     const int64_t t0 = np + i0, t1 = np + i1 - 1;
     int64_t pairs = 0, cov = 0, live = 0, full = 0, part = 0, touched = 0;
-    for (int kt = threadIdx.x; kt < G.nkt; kt += CT) {
-        const int64_t j0 = (int64_t)kt * a.tile_k, j1 = min(G.nk, j0 + a.tile_k);
-        int64_t count = 0;
-        for (int64_t j = j0; j < j1; j++) count += overlap(key_range(a, G.NS, g, j), t0, t1);
-        const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);
-        const int c = count == 0 ? 0 : (count == area ? 1 : 2);
-        a.cls[(int64_t)row * G.nkt + kt] = (uint8_t)c;
-        pairs += count;
-        if (c) {
-            cov += area;
-            live++;
-            full += c == 1;
-            part += c == 2;
+    // four consecutive lanes share a key tile, a quarter of its keys each; the
+    // quarter sums are added across them (every lane runs every round)
+    for (int base = 0; base < G.nkt * 4; base += CT) {
+        const int item = base + threadIdx.x, kt = item >> 2, qu = item & 3;
+        int64_t count = 0, j0 = 0, j1 = 0;
+        if (kt < G.nkt) {
+            j0 = (int64_t)kt * a.tile_k;
+            j1 = min(G.nk, j0 + a.tile_k);
+            const int64_t span = (a.tile_k + 3) / 4;
+            const int64_t q0 = j0 + qu * span, q1 = min(j1, q0 + span);
+            for (int64_t j = q0; j < q1; j++) count += overlap(key_range(a, G.NS, g, j), t0, t1);
+        }
+        count += __shfl_xor(count, 1, 64);
+        count += __shfl_xor(count, 2, 64);
+        if (kt < G.nkt && qu == 0) {
+            const int64_t area = (int64_t)(i1 - i0) * (j1 - j0);
+            const int c = count == 0 ? 0 : (count == area ? 1 : 2);
+            a.cls[(int64_t)row * G.nkt + kt] = (uint8_t)c;
+            pairs += count;
+            if (c) {
+                cov += area;
+                live++;
+                full += c == 1;
+                part += c == 2;
+            }
         }
     }
     if (!a.stats) return;
