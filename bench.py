@@ -42,7 +42,49 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(scale for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--probe-coexec", action="store_true",
+                    help="only time the matrix/vector co-execution probe "
+                         "(libswa_measure.so) and print its JSON line")
     return ap.parse_args()
+
+
+def probe_coexec(torch, dev):
+    """Times one workgroup of eight waves per CU: matrix-only, vector-only and
+    both (two waves per SIMD, one of each kind), for accumulators in AGPRs or
+    arch VGPRs and exp2 or FMA vector work; overlap = (t_m + t_v - t_both) /
+    min(t_m, t_v), 1 when the shorter work hides entirely under the longer."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "causal_sliding_window_swa_amd", "libswa_measure.so"))
+    lib.swa_measure_coexec.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros(blocks * 512, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    def run(im, iv, mode, agpr, trans, reps=5):
+        call = lambda: lib.swa_measure_coexec(out.data_ptr(), blocks, im, iv, mode, agpr, trans,
+                                              ctypes.c_void_p(st.cuda_stream))
+        for _ in range(2):
+            if call() != 0:
+                raise RuntimeError("coexec probe launch failed")
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            call()
+            b.record(st)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts)
+
+    res = {"workload": "co-execution probe, %d workgroups of 512 threads" % blocks}
+    for agpr in (0, 1):
+        for trans, iv in ((1, 3200), (0, 8000)):
+            t = {m: run(4000, iv, m, agpr, trans) for m in (1, 2, 3)}
+            res["acc_%s_%s" % ("agpr" if agpr else "vgpr", "exp2" if trans else "fma")] = {
+                "matrix_ms": round(t[1], 4), "vector_ms": round(t[2], 4), "both_ms": round(t[3], 4),
+                "overlap": round((t[1] + t[2] - t[3]) / min(t[1], t[2]), 3)}
+    print(json.dumps(res), flush=True)
 
 
 def src_digest(*names):
@@ -110,6 +152,9 @@ def main():
     only = set(args.only.split(",")) if args.only else {"prefill", "gqa", "chunk", "decode",
                                                          "bwd", "sink", "variants"}
     dev = torch.device("cuda:0")
+    if args.probe_coexec:
+        probe_coexec(torch, dev)
+        return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

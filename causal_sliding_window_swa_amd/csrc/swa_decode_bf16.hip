@@ -30,6 +30,7 @@
 #include <mutex>
 
 #include "../../include/swa.h"
+#include "ring_state.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
 
     // ring state before and after the append
     const int rs = a.ring_start[b], cl = a.cache_len[b], np = a.next_pos[b];
+    const bool st_ok = ring_state_ok(rs, cl, np, W, 1);  // else: no append, no key
     RingView rv;
     rv.W = W;
     const bool full = cl == W;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
     const __bf16 *vnew = (const __bf16 *)a.v_new + kvh * D;
 
     // the range owning the new slot stores the new row into the ring
-    if (rv.s_new >= s0 && rv.s_new < s1 && tid < LPR) {
+    if (st_ok && rv.s_new >= s0 && rv.s_new < s1 && tid < LPR) {
         *(u32x4 *)((__bf16 *)a.kc + (kvh * W + rv.s_new) * D + tid * 8) = ld16(knew + tid * 8);
         *(u32x4 *)((__bf16 *)a.vc + (kvh * W + rv.s_new) * D + tid * 8) = ld16(vnew + tid * 8);
     }
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(NWV * 64) void decode_split_kernel(DecodeArgs a) {
             for (int j = 0; j < 4; j++) {
                 const int s = c0 + kb * 16 + lg * 4 + j;
                 int pos;
-                const bool ok = s < w1 && rv.valid(s, pos) && pos <= qpos && pos >= qpos - W + 1;
+                const bool ok =
+                    st_ok && s < w1 && rv.valid(s, pos) && pos <= qpos && pos >= qpos - W + 1;
                 if (!ok) sacc[kb][j] = -INFINITY;
                 mloc = fmaxf(mloc, sacc[kb][j]);
             }
@@ -347,8 +350,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     if (SINK) {
         __shared__ float red[2];
         const int W = a.W, cl = a.cache_len[b], np = a.next_pos[b];
+        const bool st_ok = ring_state_ok(a.ring_start[b], cl, np, W, 1);
         const int cl2 = (cl == W) ? W : cl + 1;
-        const int nsink = min(a.n_sink, np + 1 - cl2);
+        const int nsink = st_ok ? min(a.n_sink, np + 1 - cl2) : 0;
         const int G = a.H / a.Hkv, g = h / G, c = threadIdx.x;
         const float qc = (float)((const __bf16 *)a.q)[(size_t)bh * D + c];
         const float c2 = a.scale * 1.4426950408889634f;
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
             osk = osk * f + e * vc;
             msk = mn;
         }
-        if (np < a.n_sink && h % G == 0) {  // slot np is not read in this step
+        if (st_ok && np < a.n_sink && h % G == 0) {  // slot np is not read in this step
             ((__bf16 *)a.sk)[(sbase + np) * D + c] = ((const __bf16 *)a.k_new)[((size_t)b * a.Hkv + g) * D + c];
             ((__bf16 *)a.sv)[(sbase + np) * D + c] = ((const __bf16 *)a.v_new)[((size_t)b * a.Hkv + g) * D + c];
         }
@@ -396,6 +400,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     ((__bf16 *)a.o)[(size_t)bh * D + threadIdx.x] = (__bf16)((L > 0.f) ? O / L : 0.f);
     if (!SINK && h == 0 && threadIdx.x == 0) {
         const int W = a.W, rs = a.ring_start[b], cl = a.cache_len[b];
+        if (!ring_state_ok(rs, cl, a.next_pos[b], W, 1)) return;
         const bool full = cl == W;
         a.ring_start[b] = full ? (rs + 1) % W : rs;
         a.cache_len[b] = full ? W : cl + 1;
@@ -410,6 +415,7 @@ __global__ void decode_state_kernel(int32_t *ring_start, int32_t *cache_len, int
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
     const int rs = ring_start[b], cl = cache_len[b];
+    if (!ring_state_ok(rs, cl, next_pos[b], W, 1)) return;
     const bool full = cl == W;
     ring_start[b] = full ? (rs + 1) % W : rs;
     cache_len[b] = full ? W : cl + 1;

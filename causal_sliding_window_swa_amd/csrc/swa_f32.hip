@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "ring_state.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -72,6 +73,8 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
     const int rs = (MODE == 1) ? a.ring_start[b] : 0;
     const int cl = (MODE == 1) ? a.cache_len[b] : 0;
     const int np = (MODE == 1) ? a.next_pos[b] : 0;
+    // a chunk over an unusable ring state sees no key
+    const bool st_ok = MODE == 0 || ring_state_ok(rs, cl, np, W, nq);
     const size_t kvh = (size_t)b * a.Hkv + g;
     // linear key row t: kvh row t, or token cub + t in the packed layout
     const size_t krs = pk ? (size_t)a.Hkv * d : (size_t)d;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64) void tile_f32_kernel(AttnArgs a) {
         RowState<DMAX> st;
         st.init(qrow, d);
         const int qpos = ((MODE == 1) ? np : 0) + i;
-        if (i < qlen) {
+        if (i < qlen && st_ok) {
             for (int e = e0; e < e1; e++) {
                 const int kt = a.col[e];
                 const int j1 = min(nk, (kt + 1) * a.tile_k);
@@ -145,6 +148,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     const int d = a.d, W = a.W;
     const int g = h / (a.H / a.Hkv);
     const int rs = a.ring_start[b], cl = a.cache_len[b], np = a.next_pos[b];
+    const bool st_ok = ring_state_ok(rs, cl, np, W, 1);  // else: no append, no key
     const bool full = cl == W;
     const int rs2 = full ? (rs + 1) % W : rs;
     const int cl2 = full ? W : cl + 1;
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
         int r = s - rs2;
         r += (r < 0) ? W : 0;
         const int pos = np + 1 - cl2 + r;
-        if (r < cl2 && pos <= qpos && pos >= qpos - W + 1)
+        if (st_ok && r < cl2 && pos <= qpos && pos >= qpos - W + 1)
             st.add(kring + (size_t)s * d, vring + (size_t)s * d, d, a.scale);
     }
     // attention sinks ("Sparse attention taxonomy" §3.2): positions below
@@ -165,12 +169,12 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     // appended at a sink position is copied there (that slot is not read in
     // this step, since the ring still holds it)
     if (a.n_sink > 0) {
-        const int nsink = min(a.n_sink, np + 1 - cl2);
+        const int nsink = st_ok ? min(a.n_sink, np + 1 - cl2) : 0;
         const float *ks = (const float *)a.sk + ((size_t)b * a.Hkv + g) * a.n_sink * d;
         const float *vs = (const float *)a.sv + ((size_t)b * a.Hkv + g) * a.n_sink * d;
         for (int p = threadIdx.x; p < nsink; p += 64)
             st.add(ks + (size_t)p * d, vs + (size_t)p * d, d, a.scale);
-        if (np < a.n_sink && h % (a.H / a.Hkv) == 0) {
+        if (st_ok && np < a.n_sink && h % (a.H / a.Hkv) == 0) {
             const float *kn = (const float *)a.k_new + ((size_t)b * a.Hkv + g) * d;
             const float *vn = (const float *)a.v_new + ((size_t)b * a.Hkv + g) * d;
             float *kd = (float *)a.sk + (((size_t)b * a.Hkv + g) * a.n_sink + np) * d;

@@ -12,6 +12,7 @@
 // mod W; when Tq > W only the last W rows survive.
 #include <hip/hip_runtime.h>
 
+#include "ring_state.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(256) void ring_write_kernel(CommitArgs a, int t0) {
     const int g = (int)((r / nt) % a.Hkv);
     const int b = (int)(r / ((long)nt * a.Hkv));
     const int W = a.W;
+    if (!ring_state_ok(a.ring_start[b], a.cache_len[b], a.next_pos[b], W, a.Tq)) return;
     const int slot = (int)(((int64_t)a.ring_start[b] + a.cache_len[b] + t) % W);
     const size_t kvh = (size_t)b * a.Hkv + g;
     const size_t src = (kvh * a.Tq + t) * P + pc, dst = (kvh * W + slot) * P + pc;
@@ -49,6 +51,7 @@ __global__ void ring_state_kernel(int32_t *ring_start, int32_t *cache_len, int32
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
     const int64_t rs = ring_start[b], cl = cache_len[b], np = next_pos[b];
+    if (!ring_state_ok((int)rs, (int)cl, (int)np, W, Tq)) return;
     const int64_t cl2 = (cl + Tq < W) ? cl + Tq : W;
     ring_start[b] = (int32_t)((rs + Tq + cl - cl2) % W);
     cache_len[b] = (int32_t)cl2;
@@ -60,6 +63,7 @@ __global__ void ring_state_kernel(int32_t *ring_start, int32_t *cache_len, int32
 // copied to sink slot next_pos + t.  grid (min(Tq, n_sink), Hkv, B).
 __global__ void sink_write_kernel(CommitArgs a) {
     const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (!ring_state_ok(a.ring_start[b], a.cache_len[b], a.next_pos[b], a.W, a.Tq)) return;
     const int64_t pos = (int64_t)a.next_pos[b] + t;
     if (pos >= a.n_sink) return;
     const size_t row_bytes = (size_t)a.d * a.elem_bytes;

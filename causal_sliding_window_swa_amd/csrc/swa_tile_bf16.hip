@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "ring_state.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -282,7 +283,9 @@ void tile_kernel(AttnArgs a) {
         for (int e = 0; e < 16; e++) oacc[db][e] = 0.f;
 
     const int mrow = b * nqt + qt;
-    const int e0 = a.row_ptr[mrow], e1 = a.row_ptr[mrow + 1];
+    // a chunk over an unusable ring state visits no key tile (output 0)
+    const bool st_ok = MODE == 0 || ring_state_ok(kp.rs, kp.cl, kp.np, a.W, nq);
+    const int e0 = a.row_ptr[mrow], e1 = st_ok ? a.row_ptr[mrow + 1] : e0;
     const int qpos = qbase + myrow;
     const bool qvalid = myrow < qlen;
     const int nlin_full = nrows / BN;  // linear tiles lying fully inside the data

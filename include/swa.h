@@ -242,6 +242,11 @@ int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len, 
  * keeps them); new tokens at positions below n_sink are copied there first,
  * and every query also sees each position below n_sink (at or before its
  * own) once, from the sink cache.  n_sink == 0: the sink pointers are ignored.
+ * The ring state lives on the device, so the host cannot check it: the
+ * kernels do, per request.  A request whose state is unusable (ring_start
+ * outside [0, W), cache_len outside [0, W], next_pos < 0, or next_pos + Tq
+ * beyond INT32_MAX) writes nothing to its ring, sink cache or
+ * state, and its output is zero; the other requests are unaffected.
  * Supported: as swa_fwd (W * d * 2 < 2^31 for bf16), plus W % tile_k == 0
  * and 1 <= Tq <= W.
  * Errors: as swa_fwd, plus SWA_EINVAL for n_sink < 0 or NULL / misaligned
@@ -297,6 +302,9 @@ size_t swa_decode_workspace_size(int B, int H, int d, int W);
  * query also attends over the sink positions the ring no longer holds
  * (below next_pos + 1 - cache_len after the append).  n_sink == 0: the sink
  * pointers are ignored.
+ * Device ring state as swa_prefill_chunk with Tq = 1: a request whose state is
+ * unusable (including next_pos == INT32_MAX) appends nothing, keeps its state
+ * and gets a zero output.
  * Supported: SWA_BF16 with d in {64, 128}, H / Hkv in {1, 2, 4, 8}; SWA_F32 with d a
  * multiple of 4 in [4, 128].
  * Errors: as swa_fwd, plus SWA_EINVAL when ws_bytes is too small. */
