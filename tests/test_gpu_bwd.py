@@ -102,3 +102,15 @@ def test_bwd_prefill_workload_full():
     the whole workload."""
     inp = synth.gen_bwd(1, 32, 32, 8192, 128, seed=11, std=0.5)
     compare_full(inp, 512, 128, 64, "prefill workload")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tq", [128, 64])
+@pytest.mark.parametrize("W", [17, 333])
+def test_bwd_bf16_tk128(d, tq, W):
+    """Metadata with 128-key tiles (which the forward takes): the backward
+    runs its fp32-arithmetic kernels on bf16 data (the MFMA kernels take
+    64-key tiles), against the same oracle and bars."""
+    inp = synth.gen_bwd(2, 4, 2, 333, d, seed=700 + W, std=0.5, len_lo=150, len_hi=333)
+    inp["q_len"][0] = 333
+    compare_full(inp, W, tq, 128, "bf16 tk128 d=%d tq=%d W=%d" % (d, tq, W))
