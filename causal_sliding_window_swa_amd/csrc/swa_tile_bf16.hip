@@ -43,7 +43,13 @@
 //     and V^T from LDS with ds_read_b64_tr_b16, which transposes 4x4 blocks of
 //     16-bit values across lanes, so V stays row-major in LDS;
 //   * inside a partial tile a wave skips a 32-key half in which none of its 32
-//     rows sees any key (finer than the metadata, same result).
+//     rows sees any key, and leaves unmasked a half that all of them see
+//     whole (finer than the metadata, same result);
+//   * the plain forward starts its first K/V load before the query rows and
+//     the metadata row are read (the first key tile follows from the tile's
+//     first row; the metadata's first entry is checked);
+//   * the chunk checks its request's device ring state first; an unusable one
+//     visits no key tile.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
