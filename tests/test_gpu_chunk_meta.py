@@ -77,15 +77,17 @@ def test_chunk_workload(S, tq, tk):
     assert ref["keys_touched"] == 8 * 4607 or S > 0
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_chunk_stream_with_device_metadata(dtype):
+@pytest.mark.parametrize("dtype,tiles", [("bf16", (128, 64)), ("bf16", (128, 128)),
+                                         ("bf16", (64, 128)), ("f32", (16, 16))])
+def test_chunk_stream_with_device_metadata(dtype, tiles):
     """Six chunk steps of sizes 37, 64, 128, 5, 64, 100 from rings partly
     filled, each preceded by the device metadata build on the same stream and
     no host copy of the ring state: every step's output, and the rings and
-    state at the end, against the oracle run step by step."""
+    state at the end, against the oracle run step by step (bf16 at 64- and
+    128-key tiles)."""
     W = 256
     d = 128 if dtype == "bf16" else 20
-    tq, tk = (128, 64) if dtype == "bf16" else (16, 16)
+    tq, tk = tiles
     B, H, Hkv = 3, 8, 2
     init = synth.gen_chunk(B, H, Hkv, 1, W, d, seed=21, std=0.5, dtype=dtype, p=[0] * B)
     init["cache_len"][:] = torch.tensor([0, 100, W], dtype=torch.int32)

@@ -169,3 +169,33 @@ def test_chunk_workload_tk128_full():
                       f64(inp["v_cache"]), inp["ring_start"].numpy(), inp["cache_len"].numpy(),
                       inp["next_pos"].numpy(), 4096, 1 / math.sqrt(128))[0]
     check(o, ro, "chunk workload tk128")
+
+
+@pytest.mark.parametrize("H,Hkv", [(3, 3), (8, 1), (16, 2), (6, 3)])
+@pytest.mark.parametrize("tk", [64, 128])
+def test_fwd_group_sizes(H, Hkv, tk):
+    """Query heads per KV head G = 1 (odd head count), 2 and 8, at both key
+    tilings, with padded lengths: every output against the oracle."""
+    inp = synth.gen_fwd(2, H, Hkv, 333, 128, seed=40 + H + tk, std=0.5, len_lo=100, len_hi=333)
+    L = inp["q_len"].numpy()
+    dev = {x: inp[x].to(DEV) for x in ("q", "k", "v")}
+    o, _ = fwd(dev, 100, 128, tk, L)
+    ref = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 100, 1 / math.sqrt(128),
+                     q_len=L)
+    check(o, ref, "H=%d Hkv=%d tk=%d" % (H, Hkv, tk))
+
+
+@pytest.mark.parametrize("tk", [64, 128])
+def test_chunk_group_size_8(tk):
+    """A chunk with 8 query heads per KV head (H = 16, Hkv = 2) at both key
+    tilings: output, rings and state against the oracle."""
+    W, d, Tq = 256, 128, 100
+    inp, sk, sv = _chunk_inputs(3, 16, 2, Tq, W, d, 0, seed=77 + tk)
+    o, dev, _, _ = run_chunk(inp, sk, sv, W, 128, tk, 0)
+    ro, kc, vc, rs, cl, npos = oracle.chunk(
+        f64(inp["q"]), f64(inp["k_new"]), f64(inp["v_new"]), f64(inp["k_cache"]),
+        f64(inp["v_cache"]), inp["ring_start"].numpy(), inp["cache_len"].numpy(),
+        inp["next_pos"].numpy(), W, 1 / math.sqrt(d))[:6]
+    check(o, ro, "chunk G=8 tk=%d" % tk)
+    assert np.array_equal(f64(dev["k_cache"]), kc) and np.array_equal(f64(dev["v_cache"]), vc)
+    assert np.array_equal(dev["next_pos"].cpu().numpy(), npos)
