@@ -352,6 +352,16 @@ def main():
         w3, e3, _ = timed(f3, max(3, K // 10), 2)
         out["gqa"] = dict(wall_ms=w3, kernel_ms=e3, flops=4.0 * d3 * m3["valid_pairs"] * H3)
         log("gqa: wall %.3f ms, event %.3f ms" % (w3, e3))
+        # 256-row query tiles: the eight-wave kernel whose wave groups
+        # alternate matrix and vector work (swa_pp_bf16.hip)
+        m3b = swa.swa_blockmask_build(B3, N3, N3, 4096, 256, 64, q_len=L, k_len=L)
+        md3b = swa.meta_to_device(m3b, dev)
+        f3b = lambda: swa.swa_fwd(q3, k3, v3, o3, 4096, md3b, q_len=ql3)
+        w3b, e3b, _ = timed(f3b, max(3, K // 10), 2)
+        out["gqa_tile256"] = dict(wall_ms=w3b, kernel_ms=e3b, flops=out["gqa"]["flops"],
+                                  live=len(m3b["col"]))
+        log("gqa tiles 256x64: wall %.3f ms, event %.3f ms" % (w3b, e3b))
+        del md3b
         # the same sequences packed token-major without padding (swa_fwd_varlen)
         lens = [int(x) for x in L]
         pk = [torch.cat([t[b, :, :n].transpose(0, 1) for b, n in enumerate(lens)]).contiguous()
@@ -704,6 +714,17 @@ def main():
                                "ms_per_step": round(g3["wall_ms"], 4),
                                "kernel_ms": round(g3["kernel_ms"], 4),
                                "useful_GFLOP": round(g3["flops"] / 1e9, 3)}
+    if "gqa_tile256" in out:
+        g4 = out["gqa_tile256"]
+        t = g4["flops"] / (g4["wall_ms"] * 1e-3) / 1e12
+        line["prefill_gqa_tile256"] = {"workload": "the GQA workload with 256x64 tiles (%d live "
+                                                   "tiles; one eight-wave workgroup per query "
+                                                   "tile, two wave groups alternating matrix "
+                                                   "and vector work)" % g4["live"],
+                                       "TFLOP_per_s": round(t, 2),
+                                       "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                       "ms_per_step": round(g4["wall_ms"], 4),
+                                       "kernel_ms": round(g4["kernel_ms"], 4)}
     if "gqa_packed" in out:
         gp = out["gqa_packed"]
         t = gp["flops"] / (gp["wall_ms"] * 1e-3) / 1e12

@@ -54,21 +54,34 @@ int check_span(const char *fn, swa_dtype dt, long long rows, long long row_bytes
     return SWA_OK;
 }
 
-int check_tiles(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
+// bf16 forward tiles: (64 or 128) x (64 or 128), or 256 x 64 at d = 128
+int check_tiles(const char *fn, swa_dtype dt, int d, int tile_q, int tile_k) {
     if (tile_q < 1 || tile_k < 1)
         return fail(SWA_EINVAL, "%s: tiles must be >= 1 (%d, %d)", fn, tile_q, tile_k);
+    if (dt == SWA_BF16 && tile_q == 256) {
+        if (d != 128 || tile_k != 64)
+            return fail(SWA_EUNSUPPORTED, "%s: bf16 tile_q = 256 takes d = 128 and tile_k = 64, "
+                        "got d=%d tile_k=%d", fn, d, tile_k);
+        return SWA_OK;
+    }
     if (dt == SWA_BF16 && !((tile_q == 128 || tile_q == 64) && (tile_k == 64 || tile_k == 128)))
-        return fail(SWA_EUNSUPPORTED, "%s: bf16 kernels take tile_q in {64, 128} and tile_k in "
-                    "{64, 128}, got (%d, %d)", fn, tile_q, tile_k);
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 kernels take tile_q in {64, 128, 256} and tile_k "
+                    "in {64, 128}, got (%d, %d)", fn, tile_q, tile_k);
     return SWA_OK;
 }
 
-// the MFMA backward kernels take 64-key tiles only
-int check_tiles_bwd(const char *fn, swa_dtype dt, int tile_q, int tile_k) {
-    int rc = check_tiles(fn, dt, tile_q, tile_k);
-    if (rc == SWA_OK && dt == SWA_BF16 && tile_k != 64)
-        return fail(SWA_EUNSUPPORTED, "%s: bf16 backward takes tile_k = 64, got %d", fn, tile_k);
+// the MFMA backward kernels take 64- or 128-row and 64-key tiles only
+int check_tiles_bwd(const char *fn, swa_dtype dt, int d, int tile_q, int tile_k) {
+    int rc = check_tiles(fn, dt, d, tile_q, tile_k);
+    if (rc == SWA_OK && dt == SWA_BF16 && (tile_k != 64 || tile_q == 256))
+        return fail(SWA_EUNSUPPORTED, "%s: bf16 backward takes tile_q in {64, 128} and "
+                    "tile_k = 64, got (%d, %d)", fn, tile_q, tile_k);
     return rc;
+}
+
+// the bf16 forward kernel for the tile shape (256-row tiles: swa_pp_bf16.hip)
+hipError_t launch_fwd_bf16(const swa::AttnArgs &a, hipStream_t s) {
+    return a.tile_q == 256 ? swa::launch_pp_bf16(a, s) : swa::launch_tile_bf16(a, s);
 }
 
 int launched(const char *fn, hipError_t e) {
@@ -91,7 +104,7 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     if (N < 1) return fail(SWA_EINVAL, "%s: N=%d must be >= 1", fn, N);
     if (N > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_tiles(fn, dt, d, tile_q, tile_k))) return rc;
     if ((rc = check_span(fn, dt, N, 2LL * d))) return rc;
     const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
@@ -111,7 +124,7 @@ extern "C" int swa_fwd(swa_dtype dt, int B, int H, int Hkv, int N, int d, int W,
     a.n_sink = n_sink;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
-    return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
+    return launched(fn, dt == SWA_BF16 ? launch_fwd_bf16(a, s) : swa::launch_tile_f32(a, s));
 }
 
 extern "C" int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, int max_len,
@@ -130,7 +143,7 @@ extern "C" int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
                     total, max_len);
     if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_tiles(fn, dt, d, tile_q, tile_k))) return rc;
     if ((rc = check_span(fn, dt, max_len, 2LL * d * Hkv))) return rc;
     const void *ptrs[] = {q, k, v, o, row_ptr_dev, col_dev};
     const char *names[] = {"q", "k", "v", "o", "row_ptr", "col"};
@@ -151,7 +164,7 @@ extern "C" int swa_fwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
     a.n_sink = n_sink;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
-    return launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s) : swa::launch_tile_f32(a, s));
+    return launched(fn, dt == SWA_BF16 ? launch_fwd_bf16(a, s) : swa::launch_tile_f32(a, s));
 }
 
 extern "C" size_t swa_bwd_workspace_size(int B, int H, int N) {
@@ -219,7 +232,7 @@ extern "C" int swa_bwd_varlen(swa_dtype dt, int B, int H, int Hkv, int total, in
                     total, max_len);
     if (max_len > INT_MAX - W) return fail(SWA_EINVAL, "%s: positions overflow int32", fn);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if ((rc = check_tiles_bwd(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_tiles_bwd(fn, dt, d, tile_q, tile_k))) return rc;
     // query-side rows are H * d elements apart (the wider of the two strides)
     if ((rc = check_span(fn, dt, max_len, 2LL * d * H))) return rc;
     const void *ptrs[] = {q, k, v, o, dout, lse_dev, dq, dk, dv, workspace, row_ptr_dev, col_dev};
@@ -263,7 +276,7 @@ extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, in
     if (Tq < 1 || Tq > W) return fail(SWA_EINVAL, "%s: need 1 <= Tq <= W (Tq=%d W=%d)", fn, Tq, W);
     if (n_sink < 0) return fail(SWA_EINVAL, "%s: n_sink=%d < 0", fn, n_sink);
     if ((rc = check_dtype_d(fn, dt, d))) return rc;
-    if ((rc = check_tiles(fn, dt, tile_q, tile_k))) return rc;
+    if ((rc = check_tiles(fn, dt, d, tile_q, tile_k))) return rc;
     if (W % tile_k != 0)
         return fail(SWA_EINVAL, "%s: W=%d must be a multiple of tile_k=%d", fn, W, tile_k);
     if ((rc = check_span(fn, dt, W, 2LL * d))) return rc;
@@ -305,7 +318,7 @@ extern "C" int swa_prefill_chunk(swa_dtype dt, int B, int H, int Hkv, int Tq, in
     // every position below n_sink there); the ring commit runs after the
     // attention, which reads the old ring
     if (n_sink > 0 && (rc = launched(fn, swa::launch_sink_write(c, s)))) return rc;
-    if ((rc = launched(fn, dt == SWA_BF16 ? swa::launch_tile_bf16(a, s)
+    if ((rc = launched(fn, dt == SWA_BF16 ? launch_fwd_bf16(a, s)
                                           : swa::launch_tile_f32(a, s))))
         return rc;
     return launched(fn, swa::launch_commit(c, s));

@@ -62,6 +62,8 @@ struct CommitArgs {
 // bf16 MFMA tile loop (swa_tile_bf16.hip): d in {64,128}, tile_q in {64,128},
 // tile_k in {64,128} (a 128-key tile is staged as two 64-key halves).
 hipError_t launch_tile_bf16(const AttnArgs &a, hipStream_t s);
+// 256-row query tiles, head dim 128, 64-key tiles (swa_pp_bf16.hip)
+hipError_t launch_pp_bf16(const AttnArgs &a, hipStream_t s);
 // fp32 reference-grade kernels (swa_f32.hip): any tiles, d % 4 == 0, d <= 128.
 hipError_t launch_tile_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);

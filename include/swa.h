@@ -131,9 +131,12 @@ int swa_blockmask_build(int B, int nq, int nk_lin, int W, int n_sink, int tile_q
  * Supported: SWA_BF16 with d in {64, 128}, tile_q in {64, 128}, tile_k in
  * {64, 128} (a 128-key tile is streamed as two 64-key halves; coarser tiles
  * halve the metadata but can cover more masked pairs, "Weight sparsity vs
- * attention sparsity" (AI-infra KB) §04), and N * d * 2 < 2^31 (one head's K
- * rows are addressed with 32-bit offsets); SWA_F32 with d a multiple of 4 in
- * [4, 128] and any tiles.
+ * attention sparsity" (AI-infra KB) §04), or tile_q = 256 with d = 128 and
+ * tile_k = 64 (one eight-wave workgroup per query tile whose two wave groups
+ * alternate matrix and vector work; the same outputs as (128, 64) bit for
+ * bit), and N * d * 2 < 2^31 (one head's K rows are addressed with 32-bit
+ * offsets); SWA_F32 with d a multiple of 4 in [4, 128] and any tiles.
+ * Other bf16 tiles: SWA_EUNSUPPORTED.
  * W >= N is legal (dense causal).
  * lse_dev: NULL, or device fp32 [B][H][N] that receives each row's natural-log
  * log-sum-exp of its visible scaled scores (-inf for rows that see no key),

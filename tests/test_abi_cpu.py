@@ -71,6 +71,11 @@ def test_fwd_validation_codes():
     assert _fwd(tq=32) == swa.SWA_EUNSUPPORTED
     assert _fwd(tk=32) == swa.SWA_EUNSUPPORTED
     assert _fwd(tk=256) == swa.SWA_EUNSUPPORTED
+    # 256-row query tiles: head dim 128 and 64-key tiles only
+    assert _fwd(tq=256, d=64) == swa.SWA_EUNSUPPORTED
+    assert _fwd(tq=256, tk=128) == swa.SWA_EUNSUPPORTED
+    assert "tile_q = 256" in swa.swa_last_error()
+    assert _fwd(tq=512) == swa.SWA_EUNSUPPORTED
     assert _fwd(ptr=0) == swa.SWA_EINVAL
     assert _fwd(ptr=8) == swa.SWA_EINVAL  # misaligned
     assert _fwd(dt=7) == swa.SWA_EINVAL
@@ -143,6 +148,7 @@ def test_bwd_varlen_validation_codes():
     assert _bwd_varlen(d=96) == swa.SWA_EUNSUPPORTED
     assert _bwd_varlen(tq=32) == swa.SWA_EUNSUPPORTED
     assert _bwd_varlen(tk=128) == swa.SWA_EUNSUPPORTED
+    assert _bwd_varlen(tq=256) == swa.SWA_EUNSUPPORTED  # a forward-only tile shape
     # workspace: fp32 row values [total][H]
     assert _bwd_varlen(ws=100 * 4 * 4 - 1) == swa.SWA_EINVAL
     assert "workspace" in swa.swa_last_error()
