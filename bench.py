@@ -724,7 +724,9 @@ def main():
                                        "TFLOP_per_s": round(t, 2),
                                        "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                        "ms_per_step": round(g4["wall_ms"], 4),
-                                       "kernel_ms": round(g4["kernel_ms"], 4)}
+                                       "kernel_ms": round(g4["kernel_ms"], 4),
+                                       "counters": counter_summary(
+                                           "gqa_tile256", src_digest("swa_pp_bf16.hip"))}
     if "gqa_packed" in out:
         gp = out["gqa_packed"]
         t = gp["flops"] / (gp["wall_ms"] * 1e-3) / 1e12
