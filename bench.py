@@ -398,9 +398,9 @@ def main():
         B4, H4, Tq, d4 = inp["q"].shape
         W4 = 4096
         p = inp["next_pos"].numpy()
+        inp_rs, inp_cl = inp["ring_start"].numpy(), inp["cache_len"].numpy()
         m4 = swa.swa_blockmask_build(B4, Tq, Tq, W4, tq, tk, q_start=p, k_start=p, W_ring=W4,
-                                     ring_start=inp["ring_start"].numpy(),
-                                     cache_len=inp["cache_len"].numpy(), next_pos=p)
+                                     ring_start=inp_rs, cache_len=inp_cl, next_pos=p)
         md4 = swa.meta_to_device(m4, dev)
         dv = {x: inp[x].to(dev) for x in inp}
         # the ring state as three rows of one tensor, so that a step's reset is
@@ -423,6 +423,17 @@ def main():
         out["chunk"] = dict(wall_ms=w4, kernel_ms=e4, flops=4.0 * d4 * m4["valid_pairs"] * H4,
                             keys_touched_per_request=m4["keys_touched"] // B4)
         log("chunk: wall %.3f ms, event %.3f ms" % (w4, e4))
+        # 256-row query tiles (swa_pp_bf16.hip)
+        m4b = swa.swa_blockmask_build(B4, Tq, Tq, W4, 256, 64, q_start=p, k_start=p, W_ring=W4,
+                                      ring_start=inp_rs, cache_len=inp_cl, next_pos=p)
+        md4b = swa.meta_to_device(m4b, dev)
+        f4b = lambda: swa.swa_prefill_chunk(dv["q"], dv["k_new"], dv["v_new"], dv["k_cache"],
+                                            dv["v_cache"], dv["ring_start"], dv["cache_len"],
+                                            dv["next_pos"], o4, W4, md4b)
+        w4b, e4b, _ = timed(f4b, max(5, K // 5), 2, reset=reset4)
+        out["chunk_tile256"] = dict(wall_ms=w4b, kernel_ms=e4b, flops=out["chunk"]["flops"],
+                                    live=len(m4b["col"]))
+        log("chunk tiles 256x64: wall %.3f ms, event %.3f ms" % (w4b, e4b))
         # a real stream of chunk steps: the ring moves every step, so the
         # block metadata is rebuilt before each one (the figure above resets
         # the ring state to reuse one build).  (a) on the device, in stream
@@ -747,6 +758,17 @@ def main():
                                        "TFLOP_per_s": round(t, 2),
                                        "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                        "ms_per_step": round(gb["wall_ms"], 4)}
+    if "chunk_tile256" in out:
+        c5 = out["chunk_tile256"]
+        t = c5["flops"] / (c5["wall_ms"] * 1e-3) / 1e12
+        line["chunk_tile256"] = {"workload": "the chunk workload with 256x64 tiles (%d live tiles; "
+                                             "one eight-wave workgroup per query tile)" % c5["live"],
+                                 "TFLOP_per_s": round(t, 2),
+                                 "pct_of_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                 "ms_per_step": round(c5["wall_ms"], 4),
+                                 "kernel_ms": round(c5["kernel_ms"], 4),
+                                 "counters": counter_summary(
+                                     "chunk_tile256", src_digest("swa_pp_bf16.hip"))}
     if "chunk_sink" in out:
         cs = out["chunk_sink"]
         t = cs["flops"] / (cs["wall_ms"] * 1e-3) / 1e12

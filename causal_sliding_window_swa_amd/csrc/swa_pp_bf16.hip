@@ -13,16 +13,18 @@
 // request); waves 0-3 (group 0) own rows 0-127, waves 4-7 (group 1) rows
 // 128-255, 32 rows per wave, so each SIMD runs one wave of each group.  Every
 // wave walks the same key tiles; step j of a wave is
-//   MFMA slot:  the loads of its share of K tile j+2 and V tile j+1, then
+//   MFMA part:  the loads of its share of K tile j+2 and V tile j+1, then
 //               O^T += V^T P^T of tile j-1 and S^T = K Q^T of tile j
-//   barrier
-//   VALU slot:  P = exp2(S c - m_ref) of tile j (the softmax) and the
+//   VALU part:  P = exp2(S c - m_ref) of tile j (the softmax) and the
 //               masking state of tile j+1
-//   barrier
-// and group 1 runs one barrier behind group 0.  Between any two barriers one
-// wave of each SIMD therefore issues matrix work while the other issues the
-// softmax's vector work, which the SIMD overlaps; with two independent
-// workgroups per CU the two waves' phases drift into line and overlap little.
+// with one workgroup barrier per step: group 0 meets it after its VALU part,
+// group 1 after its MFMA part.  Between two barriers group 0 runs MFMA part
+// j+1 and then VALU part j+1 while group 1 runs VALU part j and then MFMA
+// part j+1, so one wave of each SIMD issues matrix work while the other
+// issues the softmax's vector work, which the SIMD overlaps (with two
+// independent workgroups per CU the two waves' phases drift into line and
+// overlap little); the point where the two swap floats, so a part that runs
+// long on one SIMD does not hold up the other seven waves.
 // The per-wave order of the work (QK, softmax, PV, tile after tile) is that of
 // the 128-row loop, so are the fragments, the swizzles, the reference-max
 // softmax with its rare-case rescale and the masking; only the placement of
@@ -30,28 +32,25 @@
 //
 // Staging.  K and V tiles go from HBM straight to LDS (buffer_load_dwordx4 ...
 // lds) into four stages each (K tile t in stage t % 4, V likewise; 128 KB,
-// one workgroup per CU).  Group g loads rows 32g .. 32g+31 of each tile.  K
-// tile t is read in the MFMA slots of step t and by the rare-case recompute in
-// the VALU slots of step t, V tile t in the MFMA slots of step t+1, so the
-// stages a group loads into at the start of its MFMA slot of step j (K of
-// t = j+2, the stage of K tile j-2; V of t = j+1, the stage of V tile j-3)
-// are no longer read by anyone.  Both groups wait for their loads of step j-1
-// before the barrier that ends slot 2j+1 (group 0 at the end of its VALU
-// slot, group 1 at the end of its MFMA slot), leaving those of step j in
-// flight (vmcnt), so every load has three slots or more to land before the
-// MFMA slot of step j+1 reads it.  The barriers carry no memory fence (a
-// fence would wait for every load in flight); the waits above and the
-// program order of each wave's LDS reads before its barrier are what the
-// staging relies on.  Every step issues its loads, past the last tile from
-// an offset the buffer range check turns into zeros, so that the number of
-// loads in flight is the same on every path.  Issuing them in the MFMA slot
-// rather than the VALU slot balances the two slots (the VALU slot was the
-// longer one).
+// one workgroup per CU).  Group g loads rows 32g .. 32g+31 of each tile.
+// Between barriers p and p+1 both groups run MFMA part p, which reads K tile
+// p and V tile p-1 and loads K tile p+2 (the stage of K tile p-2) and V tile
+// p+1 (that of V tile p-3); K tile p is also read by the rare-case recompute
+// of VALU part p (group 0 in the same interval, group 1 in the next).  So a
+// stage is written only after every read of its previous tile has passed a
+// barrier.  Each wave waits for its loads of step p-1 (vmcnt, leaving those
+// of step p in flight) before the barrier that ends its step p, so every
+// tile is in LDS one barrier before the first MFMA part that reads it.  The
+// barriers carry no memory fence (a fence would wait for every load in
+// flight); these waits and the program order of each wave's LDS reads before
+// its barrier are what the staging relies on.  Every step issues its loads,
+// past the last tile from an offset the buffer range check turns into zeros,
+// so that the number of loads in flight is the same on every path.
 //
 // Metadata.  The row's tile columns and classes are read with scalar loads at
-// the end of a VALU slot for the next step (their wait then falls on the first
-// LDS wait of the MFMA slot, which waits anyway).  The masking intervals of a
-// partial tile j+1 are formed at the end of the VALU slot of step j; a half
+// the end of a VALU part for the next step (their wait then falls on the first
+// LDS wait of the MFMA part, which waits anyway).  The masking intervals of a
+// partial tile j+1 are formed at the end of the VALU part of step j; a half
 // that every row of the wave sees whole is left unmasked, and one that no row
 // of it sees is computed and masked like the rest (straight-line code
 // schedules better than the skip, and P is exactly 0 there), while a tile
@@ -100,7 +99,7 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // Workgroup barrier without a memory fence (see the header): the compiler
 // keeps memory operations on their side of it, the hardware only waits for
 // the other waves.
-__device__ __forceinline__ void slot_barrier() {
+__device__ __forceinline__ void step_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -542,28 +541,31 @@ void pp_kernel(AttnArgs a) {
     bool prv_run = false;
     if (T > 0)
         tile_state(col_of(0), cls_from(cls_word(0), 0), cur_partial, cur_live0, cur_live1, cur_m);
-    // columns of the K tile and V tile the next MFMA slot loads (the V tile
+    // columns of the K tile and V tile the next MFMA part loads (the V tile
     // is also the one after the current tile) and that tile's class dword
     int colK = col_of(2), colV = col_of(1), clsN = cls_word(1);
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (grp == 1) slot_barrier();  // group 1 runs one slot behind
 
     // step j: reads K tile j from Kc and V tile j-1 from Vp; loads K tile j+2
     // into Kd and V tile j+1 into Vd
     auto step = [&](int j, const char *Kc, const char *Vp, char *Kd, char *Vd)
         __attribute__((always_inline)) {
-        // ---- MFMA slot
+        // ---- MFMA part
         load_k(colK, Kd);
         load_v(colV, Vd);
         if (j > 0 && prv_run) pv(Vp);
         const bool run = j < T && (cur_live0 || cur_live1);
         if (run) scores(Kc, cur_partial, cur_m);
-        if (grp == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // loads of step j-1
-        slot_barrier();
-        // ---- VALU slot
+        if (grp == 1) {
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // loads of step j-1
+            step_barrier();
+        }
+        // ---- VALU part
+        __builtin_amdgcn_s_setprio(1);  // the softmax issues ahead of the other wave's MFMAs
         if (run) softmax(Kc, cur_partial, cur_m);
+        __builtin_amdgcn_s_setprio(0);
         prv_run = run;
         // (the opaque copy keeps the compiler from deriving the class test
         // right after the load, a step early, where it would wait for it)
@@ -574,8 +576,10 @@ void pp_kernel(AttnArgs a) {
         colV = colK;
         colK = col_of(j + 3);
         clsN = cls_word(j + 2);
-        if (grp == 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // loads of step j-1
-        slot_barrier();
+        if (grp == 0) {
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // loads of step j-1
+            step_barrier();
+        }
     };
     for (int j = 0; j <= T; j += 4) {
         step(j, K0, V3, K2, V1);
@@ -586,7 +590,6 @@ void pp_kernel(AttnArgs a) {
         if (j + 3 > T) break;
         step(j + 3, K3, V2, K1, V0);
     }
-    if (grp == 0) slot_barrier();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads into LDS past the last tile
 
     // ---- epilogue: O = O / l; rows without any visible key get 0.  The row
