@@ -47,7 +47,9 @@
 //     whole (finer than the metadata, same result);
 //   * the plain forward starts its first K/V load before the query rows and
 //     the metadata row are read (the first key tile follows from the tile's
-//     first row; the metadata's first entry is checked);
+//     first row; the metadata's first entry is checked), and issues the next
+//     tile's loads one per two QK MFMAs rather than all at once after the
+//     barrier, where every wave's loads queued together in the memory pipe;
 //   * the chunk checks its request's device ring state first; an unusable one
 //     visits no key tile.
 #include <hip/hip_runtime.h>
@@ -326,7 +328,39 @@ void tile_kernel(AttnArgs a) {
         const bool ragged = (kr - kp.nrt) >= nlin_full;
         const bool partial = (cls == 2) || ragged;
         __syncthreads();  // this tile is in LDS; every wave is done with the previous one
-        if (ktn >= 0) issue(ktn, nxt);
+        // The plain forward with 64-key metadata tiles spreads this wave's
+        // loads of the next tile over the QK MFMAs below (ld_next) instead of
+        // issuing them together here: issued at once by every wave after the
+        // barrier, they queue in the memory pipe and hold up each wave's first
+        // MFMAs.  After the last tile the loads still go out, from an offset
+        // past the data (zeros into the unused stage), so the MFMA blocks need
+        // no branch.  (With 128-key tiles the extra registers spill.)
+        constexpr bool spread = MODE == 0 && SUB == 1;
+        constexpr int NL = 2 * LPW;  // this wave's 1 KB loads of one K and V tile
+        static_assert(NL <= 2 * KS, "at most one load per QK MFMA");
+        const int ld_base = (ktn >= 0) ? ktn * BN * RSB : lin_bytes;
+        auto ld_next = [&](int i) __attribute__((always_inline)) {  // K, V, K, V, ...
+            const int j = i >> 1, ins = wave * LPW + j;
+            if (i & 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vlr, (lds_void *)(nxt + TILEB + ins * 1024), 16, ld_base + (int)voff[j], 0,
+                    0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    klr, (lds_void *)(nxt + ins * 1024), 16, ld_base + (int)koff[j], 0, 0, 0);
+        };
+        // load i follows QK MFMA (i + 1) * 2KS / NL - 1 of the tile's 2KS
+        auto ld_after = [&](int m) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NL; i++)
+                if ((i + 1) * 2 * KS / NL - 1 == m) ld_next(i);
+        };
+        auto ld_count = [](int m) {
+            int c = 0;
+            for (int i = 0; i < NL; i++) c += ((i + 1) * 2 * KS / NL - 1 == m) ? 1 : 0;
+            return c;
+        };
+        if (!spread && ktn >= 0) issue(ktn, nxt);
         // loads for the next tiles (after the barrier, so that its wait does
         // not include them)
         if (next_meta) {
@@ -393,14 +427,21 @@ void tile_kernel(AttnArgs a) {
                 const bool o2 = a2 <= b2 && a2 <= kb * 32 + 31 && b2 >= kb * 32;
                 live[kb] = __ballot(o1 || o2) != 0;
             }
-            if (!live[0] && !live[1]) return;
+            if (!live[0] && !live[1]) {
+                if (spread)
+#pragma unroll
+                    for (int i = 0; i < NL; i++) ld_next(i);
+                return;
+            }
         }
 
         // S^T = K Q^T: rows = keys (A from LDS), columns = this wave's queries;
         // masked scores become -inf; each chain starts from an inline zero
         // accumulator (no vector instructions to clear it)
         f32x16 sacc[2];
-        auto scores = [&]() {
+        // (with_loads: the first evaluation of the tile, which also issues
+        // the next tile's loads; the rare-case recompute does not)
+        auto scores = [&](bool with_loads) {
             auto qk_step = [&](int kb, int ks) {
                 const int r = kb * 32 + kr_row;
                 const int c = (2 * ks + hh) ^ kswz(r);
@@ -426,19 +467,42 @@ void tile_kernel(AttnArgs a) {
                     const int r = 32 + kr_row;
                     const int c = (2 * ks + hh) ^ kswz(r);
                     kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksm + r * ROWB + c * 16));
+                    if (spread && with_loads) ld_after(ks);
                 }
+                if (spread && with_loads)  // MFMA, K read, its share of the loads
+#pragma unroll
+                    for (int ks = 0; ks < KS; ks++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        if (ld_count(ks) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < KS; ks++)
+                for (int ks = 0; ks < KS; ks++) {
                     sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         kf[ks], qf[ks], ks == 0 ? f32x16{} : sacc[1], 0, 0, 0);
+                    if (spread && with_loads) ld_after(KS + ks);
+                }
+                if (spread && with_loads)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ks++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (ld_count(KS + ks) > 0)
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
             } else if (live[0]) {
                 // one half skipped: its scores only need to be finite (they are
                 // masked, the tile being partial)
+                if (spread && with_loads)
+#pragma unroll
+                    for (int i = 0; i < NL; i++) ld_next(i);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(0, ks);
                 sacc[1] = f32x16{};
             } else {
+                if (spread && with_loads)
+#pragma unroll
+                    for (int i = 0; i < NL; i++) ld_next(i);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) qk_step(1, ks);
                 sacc[0] = f32x16{};
@@ -499,14 +563,14 @@ void tile_kernel(AttnArgs a) {
             return half_swap_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
         };
         __builtin_amdgcn_s_setprio(2);
-        scores();
+        scores(true);
         __builtin_amdgcn_s_setprio(0);
         float psum = probs();
         const bool lane_vis = !partial || (b1 >= a1) || (two && b2 >= a2);
         const bool rare = psum > P_HI || (guess && lane_vis && psum < P_LO);
         if (__ballot(rare) != 0) {
             // take the real max of this tile's scores and move the reference
-            scores();
+            scores(false);
             float mloc = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
@@ -593,6 +657,9 @@ void tile_kernel(AttnArgs a) {
             tile(e, 2 * kt + 1, cls, e + 1 < e1 ? 2 * kt1 : -1, true, stage1, stage0);
         }
     }
+
+    // the plain forward's last tile loaded zeros into the free stage
+    if (MODE == 0 && SUB == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: O = O / l; rows without any visible key (padding) get 0.
     // The row log-sum-exp (natural log) of the scaled scores is
