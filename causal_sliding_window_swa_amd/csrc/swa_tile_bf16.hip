@@ -602,27 +602,39 @@ void tile_kernel(AttnArgs a) {
 
         __builtin_amdgcn_s_setprio(2);
         // O^T += V^T P^T in 16-key steps kk; the MFMA k index hh*8 + 4r + t of
-        // both operands stands for tile key 16kk + 8r + 4hh + t.
+        // both operands stands for tile key 16kk + 8r + 4hh + t.  Per live
+        // 32-key half, every V^T fragment is read before the first of its
+        // MFMAs (the scheduling barrier keeps the compiler from moving each
+        // read next to its MFMA, where every MFMA of the first key step
+        // waited out a full LDS latency).
+        auto vread = [&](int kk, int db, int r) __attribute__((always_inline)) {
+            const int row = kk * 16 + 8 * r + tr_row;
+            const int col = db * 32 + tr_col;
+            const int c = (col >> 3) ^ vswz(row);
+            const char *p = vsm + row * ROWB + c * 16 + (col & 7) * 2;
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+        };
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            if (!live[kk >> 1]) continue;
+        for (int kb = 0; kb < 2; kb++) {
+            if (!live[kb]) continue;
+            i16x4 vr[2][DB][2];
 #pragma unroll
-            for (int db = 0; db < DB; db++) {
-                i16x4 v2[2];
+            for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-                for (int r = 0; r < 2; r++) {
-                    const int row = kk * 16 + 8 * r + tr_row;
-                    const int col = db * 32 + tr_col;
-                    const int c = (col >> 3) ^ vswz(row);
-                    const char *p = vsm + row * ROWB + c * 16 + (col & 7) * 2;
-                    v2[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+                for (int db = 0; db < DB; db++)
+#pragma unroll
+                    for (int r = 0; r < 2; r++) vr[s2][db][r] = vread(2 * kb + s2, db, r);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    const u32x2 lo = __builtin_bit_cast(u32x2, vr[s2][db][0]);
+                    const u32x2 hi = __builtin_bit_cast(u32x2, vr[s2][db][1]);
+                    const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, vv), pk[2 * kb + s2], oacc[db], 0, 0, 0);
                 }
-                const u32x2 lo = __builtin_bit_cast(u32x2, v2[0]);
-                const u32x2 hi = __builtin_bit_cast(u32x2, v2[1]);
-                const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                                   pk[kk], oacc[db], 0, 0, 0);
-            }
         }
         __builtin_amdgcn_s_setprio(0);
     };
