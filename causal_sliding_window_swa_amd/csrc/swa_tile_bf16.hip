@@ -44,7 +44,9 @@
 //     16-bit values across lanes, so V stays row-major in LDS;
 //   * inside a partial tile a wave skips a 32-key half in which none of its 32
 //     rows sees any key, and leaves unmasked a half that all of them see
-//     whole (finer than the metadata, same result);
+//     whole (finer than the metadata, same result); without attention sinks
+//     the plain forward's mask tests one key interval per element (a
+//     separate instantiation), with them two;
 //   * the plain forward starts its first K/V load before the query rows and
 //     the metadata row are read (the first key tile follows from the tile's
 //     first row; the metadata's first entry is checked), and issues the next
@@ -126,7 +128,9 @@ __device__ __forceinline__ int xcd_deal(int p, int T) {
     return Tm + xcd_remap(p - Tm, T - Tm);
 }
 
-template <int MODE, int D, int NW, bool PK, int SUB>
+// SK: attention sinks may be present (else the per-element mask of the plain
+// forward tests one key interval instead of two)
+template <int MODE, int D, int NW, bool PK, int SUB, bool SK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tile_kernel(AttnArgs a) {
     constexpr int KS = D / 16;          // k-steps of the QK product
@@ -335,7 +339,7 @@ void tile_kernel(AttnArgs a) {
         // MFMAs.  After the last tile the loads still go out, from an offset
         // past the data (zeros into the unused stage), so the MFMA blocks need
         // no branch.  (With 128-key tiles the extra registers spill.)
-        constexpr bool spread = MODE == 0 && SUB == 1;
+        constexpr bool spread = MODE == 0 && (SUB == 1 || !SK);
         constexpr int NL = 2 * LPW;  // this wave's 1 KB loads of one K and V tile
         static_assert(NL <= 2 * KS, "at most one load per QK MFMA");
         const int ld_base = (ktn >= 0) ? ktn * BN * RSB : lin_bytes;
@@ -383,7 +387,7 @@ void tile_kernel(AttnArgs a) {
                 const int base = kt * BN;       // position of tile key 0
                 a1 = lo_pos - base;
                 b1 = min(qpos, qlen - 1) - base;
-                if (a.n_sink > base) {  // attention sinks: keys 0 .. n_sink-1
+                if (SK && a.n_sink > base) {  // attention sinks: keys 0 .. n_sink-1
                     two = true;
                     a2 = -base;
                     b2 = min(a.n_sink - 1, min(qpos, qlen - 1)) - base;
@@ -671,7 +675,7 @@ void tile_kernel(AttnArgs a) {
     }
 
     // the plain forward's last tile loaded zeros into the free stage
-    if (MODE == 0 && SUB == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (MODE == 0 && (SUB == 1 || !SK)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: O = O / l; rows without any visible key (padding) get 0.
     // The row log-sum-exp (natural log) of the scaled scores is
@@ -700,12 +704,17 @@ hipError_t launch_one(const AttnArgs &a, hipStream_t s) {
     const long nqt = (a.nq + 32 * NW - 1) / (32 * NW);
     const long total = nqt * a.H * a.B;
     if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (MODE == 0 && a.cu)
-        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true, SUB>), dim3((unsigned)total),
-                           dim3(NW * 64), 0, s, a);
+    const dim3 grid((unsigned)total), block(NW * 64);
+    if constexpr (MODE == 1)
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false, SUB, true>), grid, block, 0, s, a);
+    else if (a.cu && a.n_sink > 0)
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true, SUB, true>), grid, block, 0, s, a);
+    else if (a.cu)
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, true, SUB, false>), grid, block, 0, s, a);
+    else if (a.n_sink > 0)
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false, SUB, true>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false, SUB>), dim3((unsigned)total),
-                           dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((tile_kernel<MODE, D, NW, false, SUB, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
