@@ -332,13 +332,14 @@ void tile_kernel(AttnArgs a) {
         const bool ragged = (kr - kp.nrt) >= nlin_full;
         const bool partial = (cls == 2) || ragged;
         __syncthreads();  // this tile is in LDS; every wave is done with the previous one
-        // The plain forward with 64-key metadata tiles spreads this wave's
-        // loads of the next tile over the QK MFMAs below (ld_next) instead of
-        // issuing them together here: issued at once by every wave after the
-        // barrier, they queue in the memory pipe and hold up each wave's first
-        // MFMAs.  After the last tile the loads still go out, from an offset
-        // past the data (zeros into the unused stage), so the MFMA blocks need
-        // no branch.  (With 128-key tiles the extra registers spill.)
+        // The plain forward spreads this wave's loads of the next tile over
+        // the QK MFMAs below (ld_next) instead of issuing them together here:
+        // issued at once by every wave after the barrier, they queue in the
+        // memory pipe and hold up each wave's first MFMAs.  After the last
+        // tile the loads still go out, from an offset past the data (zeros
+        // into the unused stage; the buffer range check covers the whole
+        // offset), so the MFMA blocks need no branch.  (With 128-key tiles and
+        // attention sinks the extra registers spill, so that case issues here.)
         constexpr bool spread = MODE == 0 && (SUB == 1 || !SK);
         constexpr int NL = 2 * LPW;  // this wave's 1 KB loads of one K and V tile
         static_assert(NL <= 2 * KS, "at most one load per QK MFMA");
