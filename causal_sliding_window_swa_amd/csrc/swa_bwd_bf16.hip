@@ -166,7 +166,9 @@ __device__ __forceinline__ void stage_vals(const float *src, int i, int n, int s
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool PK>
+// SK: attention sinks may be present; without them the second key interval of
+// the per-element mask folds away (a call without sinks runs SK = false)
+template <int D, int NW, bool PK, bool SK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel(BwdArgs a) {
     constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2, TILEB = BN * ROWB;
@@ -281,8 +283,8 @@ void dq_kernel(BwdArgs a) {
         a2 = max(a2, 0);
         b2 = min(b2, BN - 1);
         const bool empty2 = b2 < a2;
-        const int L2 = empty2 ? -(1 << 20) : a2 - 4 * hh;
-        const uint32_t n2 = empty2 ? 0u : (uint32_t)(b2 - a2);
+        const int L2 = (!SK || empty2) ? -(1 << 20) : a2 - 4 * hh;
+        const uint32_t n2 = (!SK || empty2) ? 0u : (uint32_t)(b2 - a2);
 
         // the two 32-key halves one after the other (a loop, not unrolled): S,
         // dP and dS of one half are live at a time, which keeps the kernel
@@ -671,10 +673,14 @@ hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
     const long nkt = (a.N + BN - 1) / BN;
     const long gq = nqt * a.H * a.B, gk = nkt * a.Hkv * a.B;
     if (gq > 0x7fffffffL || gk > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (NWq == 4)
-        hipLaunchKernelGGL((dq_kernel<D, 4, PK>), dim3((unsigned)gq), dim3(256), 0, s, a);
+    if (NWq == 4 && a.n_sink > 0)
+        hipLaunchKernelGGL((dq_kernel<D, 4, PK, true>), dim3((unsigned)gq), dim3(256), 0, s, a);
+    else if (NWq == 4)
+        hipLaunchKernelGGL((dq_kernel<D, 4, PK, false>), dim3((unsigned)gq), dim3(256), 0, s, a);
+    else if (a.n_sink > 0)
+        hipLaunchKernelGGL((dq_kernel<D, 2, PK, true>), dim3((unsigned)gq), dim3(128), 0, s, a);
     else
-        hipLaunchKernelGGL((dq_kernel<D, 2, PK>), dim3((unsigned)gq), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((dq_kernel<D, 2, PK, false>), dim3((unsigned)gq), dim3(128), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((dkdv_kernel<D, PK>), dim3((unsigned)gk), dim3(256), 0, s, a);
     return hipGetLastError();
