@@ -320,13 +320,22 @@ void dq_kernel(BwdArgs a) {
                             vis ? __builtin_amdgcn_exp2f(fmaf(s[e2], c2, -lse2)) : 0.f;
                         dsk[s2][4 * r + t] = (__bf16)(p * (dp[e2] - Dr));
                     }
+            // every K^T fragment of this half's dQ MFMAs before the first of them
+            // (left to itself the compiler reads each pair just before its MFMA,
+            // which then waits out the LDS latency)
+            bf16x8 ktf[2][DB];
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
                 for (int db = 0; db < DB; db++)
-                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_frag<D>(ksm, 2 * kb2 + s2, db, tr_row, tr_col), dsk[s2], dqacc[db], 0, 0,
-                        0);
+                    ktf[s2][db] = tr_frag<D>(ksm, 2 * kb2 + s2, db, tr_row, tr_col);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+                for (int db = 0; db < DB; db++)
+                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[s2][db], dsk[s2],
+                                                                        dqacc[db], 0, 0, 0);
         }
     };
     if (e1 > e0) issue(__builtin_amdgcn_readfirstlane(v_col), stage0);
